@@ -1,0 +1,285 @@
+/*
+ * oracle.c -- plain, slow, single-threaded CPU oracle for the stable LSD
+ * radix sort, the positive-value stream compaction and the bitonic tile.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing on the product path may include, link,
+ * load or call this file: only the test suite, the smoke check and the
+ * benchmark's CPU-baseline leg use it.  It shares no code, header, table or
+ * helper with the HIP library; the two meet only through the seeded input
+ * generators and through comparisons made by the tests.
+ *
+ * What it computes, and the passages it follows:
+ *
+ *  - oracle_lsd_sort_u32: the least-significant-digit radix sort as a
+ *    sequence of stable counting sorts, one per digit, from the lowest digit
+ *    up ("CUDA 算子笔记 3", section "Radix Sort", the CPU code: zero the
+ *    counts, count each digit, turn the counts into exclusive starts, then
+ *    place each element at its digit's next free slot in input order, swap
+ *    buffers).  The textbook chapter ("第10章 并行模式：排序", 10.3 Radix Sort
+ *    算法) gives the same four steps and states that the sort is stable; the
+ *    WebGPU chapter ("WebGPU Unleashed", 4.1 래딕스 정렬) states that each
+ *    digit pass must be stable for the LSD order to be correct.  The pages
+ *    always sort all 32 bits; here a bit range [begin_bit, end_bit) selects
+ *    the ordering field and the last digit is narrowed to the bits left.
+ *    Values, when given, move with their keys (10.6 Key-Value排序).
+ *  - oracle_sort_pairs_f32: the float exercise of the same chapter (八、习题,
+ *    the IEEE 754 preprocessing question) answered by the usual
+ *    order-preserving bit transform: negative patterns are inverted, the
+ *    sign bit of non-negative patterns is set; the sort runs on the
+ *    transformed bits and the transform is undone on the way out.  Only
+ *    integer operations touch the keys.
+ *  - oracle_digit_histograms: the per-pass digit counts the multi-bit
+ *    radix sort starts from ("CUDA 算子笔记 3", section 一次处理多位, the first
+ *    kernel: one read of the keys counts every pass's digits).
+ *  - oracle_compact_positive_f32: "CUDA 算子笔记 3", section Stream
+ *    Compaction: keep the values greater than zero, in input order, at the
+ *    front of the output; the rest of the output holds zeros (the worked
+ *    example shows the zero tail); the kept count is returned.
+ *  - oracle_bitonic_tile: each run of `tile` consecutive keys is sorted on
+ *    its own by the same field, stably.  A bitonic network that compares
+ *    (field, original index) pairs -- the form used on the GPU because the
+ *    network itself is not stable ("第10章", 10.7 稳定排序 vs 不稳定排序) --
+ *    reaches exactly this result, so the oracle is the definition.
+ *
+ * Floating point: the compaction predicate is the C comparison x > 0.0f on
+ * the float value, as the pages write it.  This file must be built without
+ * -ffast-math; a pin test checks that positive subnormals are kept, which
+ * would fail if denormals were flushed in the calling process.
+ */
+#include <stdint.h>
+#include <stdlib.h>
+#include <string.h>
+
+#define ORACLE_OK 0
+#define ORACLE_BAD_ARGS (-1)
+#define ORACLE_NO_MEMORY (-2)
+
+/* The digit of `key` that starts at bit `shift` and is `width` bits wide. */
+static uint32_t digit_at(uint32_t key, int shift, int width)
+{
+    uint32_t mask = (width >= 32) ? 0xFFFFFFFFu : ((1u << width) - 1u);
+    return (key >> shift) & mask;
+}
+
+/*
+ * One stable counting-sort pass on the digit at [shift, shift + width).
+ * src/dst keys (and values when src_vals != NULL).
+ */
+static void counting_sort_pass(const uint32_t *src_keys, const uint32_t *src_vals,
+                               uint32_t *dst_keys, uint32_t *dst_vals, uint64_t n,
+                               int shift, int width, uint64_t *cnt)
+{
+    uint64_t buckets = (uint64_t)1 << width;
+    uint64_t d, j, sum;
+
+    for (d = 0; d < buckets; ++d)
+        cnt[d] = 0;
+    for (j = 0; j < n; ++j)
+        cnt[digit_at(src_keys[j], shift, width)] += 1;
+
+    /* exclusive scan: cnt[d] becomes the first output slot of digit d */
+    sum = 0;
+    for (d = 0; d < buckets; ++d) {
+        uint64_t c = cnt[d];
+        cnt[d] = sum;
+        sum += c;
+    }
+
+    /* scatter in input order: equal digits keep their relative order */
+    for (j = 0; j < n; ++j) {
+        uint32_t dg = digit_at(src_keys[j], shift, width);
+        uint64_t slot = cnt[dg];
+        cnt[dg] = slot + 1;
+        dst_keys[slot] = src_keys[j];
+        if (src_vals)
+            dst_vals[slot] = src_vals[j];
+    }
+}
+
+/*
+ * Stable LSD radix sort of (keys, vals) by bits [begin_bit, end_bit) of the
+ * key, with digits of `digit_bits` bits (1..16); the last digit is narrowed.
+ * vals_in/vals_out may both be NULL (keys only).  Inputs are not modified.
+ * Returns 0, or a negative code on bad arguments or allocation failure.
+ */
+int oracle_lsd_sort_u32(const uint32_t *keys_in, const uint32_t *vals_in,
+                        uint32_t *keys_out, uint32_t *vals_out, uint64_t n,
+                        int begin_bit, int end_bit, int digit_bits)
+{
+    uint32_t *ka, *kb, *va = NULL, *vb = NULL, *tk, *tv;
+    uint64_t *cnt;
+    int shift;
+    int pairs = (vals_in != NULL);
+
+    if (begin_bit < 0 || end_bit > 32 || begin_bit > end_bit)
+        return ORACLE_BAD_ARGS;
+    if (digit_bits < 1 || digit_bits > 16)
+        return ORACLE_BAD_ARGS;
+    if ((vals_in == NULL) != (vals_out == NULL))
+        return ORACLE_BAD_ARGS;
+    if (n == 0)
+        return ORACLE_OK;
+
+    ka = (uint32_t *)malloc(n * sizeof(uint32_t));
+    kb = (uint32_t *)malloc(n * sizeof(uint32_t));
+    cnt = (uint64_t *)malloc(((size_t)1 << digit_bits) * sizeof(uint64_t));
+    if (pairs) {
+        va = (uint32_t *)malloc(n * sizeof(uint32_t));
+        vb = (uint32_t *)malloc(n * sizeof(uint32_t));
+    }
+    if (!ka || !kb || !cnt || (pairs && (!va || !vb))) {
+        free(ka); free(kb); free(cnt); free(va); free(vb);
+        return ORACLE_NO_MEMORY;
+    }
+
+    memcpy(ka, keys_in, n * sizeof(uint32_t));
+    if (pairs)
+        memcpy(va, vals_in, n * sizeof(uint32_t));
+
+    for (shift = begin_bit; shift < end_bit; shift += digit_bits) {
+        int width = end_bit - shift;
+        if (width > digit_bits)
+            width = digit_bits;
+        counting_sort_pass(ka, va, kb, vb, n, shift, width, cnt);
+        tk = ka; ka = kb; kb = tk;
+        tv = va; va = vb; vb = tv;
+    }
+
+    memcpy(keys_out, ka, n * sizeof(uint32_t));
+    if (pairs)
+        memcpy(vals_out, va, n * sizeof(uint32_t));
+
+    free(ka); free(kb); free(cnt); free(va); free(vb);
+    return ORACLE_OK;
+}
+
+/* Order-preserving transform of an IEEE 754 binary32 bit pattern. */
+static uint32_t f32_to_order(uint32_t u)
+{
+    return (u & 0x80000000u) ? ~u : (u | 0x80000000u);
+}
+
+/* Inverse of f32_to_order. */
+static uint32_t order_to_f32(uint32_t o)
+{
+    return (o & 0x80000000u) ? (o & 0x7FFFFFFFu) : ~o;
+}
+
+void oracle_f32_to_order(const uint32_t *bits_in, uint32_t *order_out, uint64_t n)
+{
+    uint64_t i;
+    for (i = 0; i < n; ++i)
+        order_out[i] = f32_to_order(bits_in[i]);
+}
+
+void oracle_order_to_f32(const uint32_t *order_in, uint32_t *bits_out, uint64_t n)
+{
+    uint64_t i;
+    for (i = 0; i < n; ++i)
+        bits_out[i] = order_to_f32(order_in[i]);
+}
+
+/*
+ * Stable sort of float keys (given as raw bit patterns) with optional u32
+ * values.  [begin_bit, end_bit) selects bits of the transformed pattern;
+ * (0, 32) is the full IEEE 754 totalOrder.  Output keys are the original
+ * bit patterns in sorted order.
+ */
+int oracle_sort_pairs_f32(const uint32_t *key_bits_in, const uint32_t *vals_in,
+                          uint32_t *key_bits_out, uint32_t *vals_out, uint64_t n,
+                          int begin_bit, int end_bit, int digit_bits)
+{
+    uint32_t *ord;
+    uint64_t i;
+    int rc;
+
+    if (n == 0)
+        return oracle_lsd_sort_u32(key_bits_in, vals_in, key_bits_out, vals_out, 0,
+                                   begin_bit, end_bit, digit_bits);
+    ord = (uint32_t *)malloc(n * sizeof(uint32_t));
+    if (!ord)
+        return ORACLE_NO_MEMORY;
+    for (i = 0; i < n; ++i)
+        ord[i] = f32_to_order(key_bits_in[i]);
+    rc = oracle_lsd_sort_u32(ord, vals_in, key_bits_out, vals_out, n, begin_bit,
+                             end_bit, digit_bits);
+    if (rc == ORACLE_OK)
+        for (i = 0; i < n; ++i)
+            key_bits_out[i] = order_to_f32(key_bits_out[i]);
+    free(ord);
+    return rc;
+}
+
+/*
+ * Digit counts for every 8-bit pass over [begin_bit, end_bit):
+ * counts[p * 256 + d] = number of keys whose pass-p digit equals d, where
+ * pass p covers bits [begin_bit + 8p, min(begin_bit + 8p + 8, end_bit)).
+ * With transform_f32 != 0 the keys are float bit patterns and the counts
+ * are taken on their order-preserving transform.  counts must hold
+ * ceil((end_bit - begin_bit) / 8) * 256 entries.  Returns the pass count,
+ * or a negative code.
+ */
+int oracle_digit_histograms(const uint32_t *keys, uint64_t n, int begin_bit, int end_bit,
+                            int transform_f32, uint64_t *counts)
+{
+    int passes, p;
+    uint64_t i;
+
+    if (begin_bit < 0 || end_bit > 32 || begin_bit > end_bit)
+        return ORACLE_BAD_ARGS;
+    passes = (end_bit - begin_bit + 7) / 8;
+    for (i = 0; i < (uint64_t)passes * 256u; ++i)
+        counts[i] = 0;
+    for (p = 0; p < passes; ++p) {
+        int shift = begin_bit + 8 * p;
+        int width = end_bit - shift;
+        if (width > 8)
+            width = 8;
+        for (i = 0; i < n; ++i) {
+            uint32_t k = transform_f32 ? f32_to_order(keys[i]) : keys[i];
+            counts[(uint64_t)p * 256u + digit_at(k, shift, width)] += 1;
+        }
+    }
+    return passes;
+}
+
+/*
+ * Keep x > 0.0f in input order at the front of out, fill the rest with
+ * +0.0f, return the kept count.  in/out are float arrays of length n.
+ */
+uint64_t oracle_compact_positive_f32(const float *in, float *out, uint64_t n)
+{
+    uint64_t i, k = 0;
+    for (i = 0; i < n; ++i) {
+        float x = in[i];
+        if (x > 0.0f) {
+            memcpy(&out[k], &in[i], sizeof(float));
+            k += 1;
+        }
+    }
+    for (i = k; i < n; ++i)
+        out[i] = 0.0f;
+    return k;
+}
+
+/*
+ * Each run [s, min(s + tile, n)) of the keys, s = 0, tile, 2 tile, ..., is
+ * stably sorted on its own by bits [begin_bit, end_bit).
+ */
+int oracle_bitonic_tile(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n,
+                        uint64_t tile, int begin_bit, int end_bit)
+{
+    uint64_t s;
+    int rc;
+
+    if (tile == 0)
+        return ORACLE_BAD_ARGS;
+    for (s = 0; s < n; s += tile) {
+        uint64_t len = (n - s < tile) ? (n - s) : tile;
+        rc = oracle_lsd_sort_u32(keys_in + s, NULL, keys_out + s, NULL, len, begin_bit,
+                                 end_bit, 8);
+        if (rc != ORACLE_OK)
+            return rc;
+    }
+    return ORACLE_OK;
+}
