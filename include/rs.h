@@ -1,0 +1,158 @@
+/*
+ * rs.h -- C ABI of the MI355X (gfx950) stable LSD radix sort library.
+ *
+ * Entry points:
+ *   rs_sort_keys_u32        stable sort of 32-bit keys
+ *   rs_sort_pairs_u32       stable sort of 32-bit keys with 32-bit values
+ *   rs_sort_pairs_f32       stable sort of float keys (IEEE 754 total order)
+ *                           with 32-bit values
+ *   rs_compact_positive_f32 keep x > 0 in order, zero-fill the rest, count
+ *   rs_bitonic_tile         sort each run of at most 1024 keys in LDS
+ *   rs_status_string        text of a status code
+ *
+ * Common rules.
+ *  - Every data pointer is a DEVICE pointer (hipMalloc or torch CUDA tensor
+ *    storage) unless stated.  Inputs are read-only and never modified;
+ *    outputs are fully written when the call returns RS_OK.  Input, output
+ *    and temporary ranges must not overlap each other (RS_ERR_OVERLAP).
+ *  - Every data pointer must be 16-byte aligned (RS_ERR_MISALIGNED); the
+ *    kernels use 16-byte vector loads where the layout allows.
+ *  - Work is enqueued on `stream` (NULL = the null stream) and the call
+ *    returns without synchronising; the caller synchronises.
+ *  - All argument checks happen on the host before anything is enqueued: a
+ *    call that returns an error has launched nothing and written nothing.
+ *    RS_ERR_HIP reports a failed launch (hipGetLastError) after enqueueing.
+ *  - Temporary storage follows the two-call query idiom the textbook chapter
+ *    shows for library radix sorts ("第10章 并行模式：排序", 10.8 Thrust/CUB):
+ *    with d_temp == NULL the required size is written to *temp_bytes and
+ *    nothing is launched; otherwise *temp_bytes must be at least that size.
+ *    The caller owns the temp buffer and need not initialise it.  The size
+ *    depends only on n (and on whether values are sorted).
+ *  - The library keeps no mutable state between calls: concurrent calls on
+ *    different streams with different temp buffers are independent.
+ *  - n < 2^30 (RS_ERR_UNSUPPORTED_SIZE otherwise): cross-tile prefix states
+ *    hold 30-bit counts beside 2 status bits.
+ */
+#ifndef RS_H
+#define RS_H
+
+#include <stddef.h>
+#include <stdint.h>
+#include <hip/hip_runtime_api.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum rs_status {
+    RS_OK = 0,
+    RS_ERR_INVALID_VALUE = 1,    /* null pointer with n > 0, bad bit range, bad tile */
+    RS_ERR_UNSUPPORTED_SIZE = 2, /* n >= 2^30 */
+    RS_ERR_TEMP_TOO_SMALL = 3,   /* *temp_bytes below the queried size */
+    RS_ERR_OVERLAP = 4,          /* two of the buffers overlap */
+    RS_ERR_MISALIGNED = 5,       /* a pointer is not 16-byte aligned */
+    RS_ERR_HIP = 6               /* a HIP launch or runtime call failed */
+} rs_status;
+
+#define RS_MAX_N ((uint64_t)1 << 30)
+
+/*
+ * Stable LSD radix sort of keys by bits [begin_bit, end_bit).
+ *
+ * Defines: the least-significant-digit sort as one stable counting sort per
+ * 8-bit digit, lowest digit first ("CUDA 算子笔记 3", sections Radix Sort
+ * and 一次处理多位; "第10章 并行模式：排序", 10.3 Radix Sort算法; "WebGPU
+ * Unleashed", 4.1 래딕스 정렬, on why each digit pass must be stable).
+ *
+ * keys_in  [n] u32, read only.          keys_out [n] u32, written.
+ * n        element count, 0 <= n < 2^30.
+ * begin_bit, end_bit: 0 <= begin_bit <= end_bit <= 32.  The ordering field
+ *          is (key >> begin_bit) & (2^(end_bit-begin_bit) - 1); bits outside
+ *          it are carried but ignored; equal fields keep input order.
+ *          begin_bit == end_bit copies the input.
+ * d_temp, temp_bytes: see the query idiom above.
+ */
+rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n,
+                           int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
+                           hipStream_t stream);
+
+/*
+ * Stable LSD radix sort of (key, value) pairs by key bits [begin_bit,
+ * end_bit); values move with their keys ("第10章 并行模式：排序", 10.6
+ * Key-Value排序).  vals_in [n] u32 read only, vals_out [n] u32 written; the
+ * other arguments are as for rs_sort_keys_u32.
+ */
+rs_status rs_sort_pairs_u32(const uint32_t *keys_in, uint32_t *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, uint64_t n,
+                            int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
+                            hipStream_t stream);
+
+/*
+ * Stable sort of float keys with u32 values.  Keys are ordered through the
+ * order-preserving transform of their bit patterns (negative patterns
+ * inverted, the sign bit of the others set), which the textbook's float
+ * exercise asks for ("第10章 并行模式：排序", 八、习题); the result is IEEE
+ * 754 totalOrder: -NaN < -inf < ... < -0.0 < +0.0 < ... < +inf < +NaN,
+ * subnormals kept.  No float arithmetic touches a key.  [begin_bit,
+ * end_bit) selects bits of the transformed pattern; (0, 32) is the full
+ * order.  keys_out holds the original bit patterns in sorted order.
+ */
+rs_status rs_sort_pairs_f32(const float *keys_in, float *keys_out,
+                            const uint32_t *vals_in, uint32_t *vals_out, uint64_t n,
+                            int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
+                            hipStream_t stream);
+
+/*
+ * Stream compaction: out[0..k) = the inputs with x > 0.0f in input order,
+ * out[k..n) = +0.0f, *d_count = k ("CUDA 算子笔记 3", section Stream
+ * Compaction and its decoupled look-back method).  The predicate is taken
+ * on the bit pattern, so positive subnormals are kept and NaNs are not.
+ *
+ * in [n] f32 read only; out [n] f32 written; d_count: one u32 in device
+ * memory, written (0 when n == 0).  d_temp/temp_bytes: query idiom.
+ */
+rs_status rs_compact_positive_f32(const float *in, float *out, uint32_t *d_count, uint64_t n,
+                                  void *d_temp, size_t *temp_bytes, hipStream_t stream);
+
+/*
+ * Each run keys[s .. min(s + tile, n)), s = 0, tile, 2 tile, ..., is sorted
+ * on its own in LDS by a bitonic network ("gpu排序__gpu", the in-block
+ * bitonic sort of up to 1024 elements; "第10章 并行模式：排序", 10.2 Bitonic
+ * Sort) comparing (field, position) so that the result is the stable order.
+ * tile in [1, 1024]; begin_bit/end_bit as for rs_sort_keys_u32.  No temp.
+ */
+rs_status rs_bitonic_tile(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n,
+                          uint32_t tile, int begin_bit, int end_bit, hipStream_t stream);
+
+/* Static text for a status code (never NULL). */
+const char *rs_status_string(rs_status status);
+
+/*
+ * Measurement hook.  When enabled, the library brackets every kernel it
+ * launches with hipEventRecord on the call's stream and keeps the events;
+ * rs_timing_collect waits for them and returns per-launch durations.  It is
+ * process-wide and not meant for concurrent use; off by default.
+ *
+ * rs_timing_enable(1) clears previous records and starts recording;
+ * rs_timing_enable(0) stops.  rs_timing_collect writes up to `cap` records
+ * (kernel id, milliseconds) in launch order and returns the number of
+ * records held (which may exceed cap), or -1 on a HIP error.
+ */
+typedef enum rs_kernel_id {
+    RS_KERNEL_UPSWEEP = 0,      /* all passes' digit counts, one read of the keys */
+    RS_KERNEL_ONESWEEP = 1,     /* one digit pass: rank, look-back, scatter */
+    RS_KERNEL_SORT_INIT = 2,    /* clears the sort's counters and states */
+    RS_KERNEL_COMPACT_INIT = 3, /* clears the compaction's counter and states */
+    RS_KERNEL_COMPACT = 4,      /* single-pass compaction */
+    RS_KERNEL_BITONIC = 5,      /* LDS bitonic tiles */
+    RS_KERNEL_COPY = 6          /* device copy for an empty bit range */
+} rs_kernel_id;
+
+rs_status rs_timing_enable(int enable);
+int rs_timing_collect(int *kernel_ids, float *ms, int cap);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* RS_H */

@@ -1,0 +1,263 @@
+"""Python binding of the gfx950 stable LSD radix sort library (``librs.so``).
+
+The functions named ``rs_*`` mirror the C ABI in ``include/rs.h`` one for one:
+they only turn tensors or integers into device pointers and sizes, call the
+library and raise :class:`RsError` on a status other than ``RS_OK``.  Every
+step of the computation runs in the library's HIP kernels.  The convenience
+wrappers below them (``sort_keys_u32`` ...) allocate outputs and temporary
+storage with torch on the tensors' device and launch on torch's current
+stream; torch provides memory and streams only.
+
+Loading fails with an error when ``librs.so`` has not been built; there is no
+fallback implementation.
+"""
+import ctypes
+import os
+
+__all__ = [
+    "RsError", "RS_OK", "RS_ERR_INVALID_VALUE", "RS_ERR_UNSUPPORTED_SIZE",
+    "RS_ERR_TEMP_TOO_SMALL", "RS_ERR_OVERLAP", "RS_ERR_MISALIGNED", "RS_ERR_HIP",
+    "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_compact_positive_f32",
+    "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
+    "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "compact_positive_f32", "bitonic_tile",
+    "library_path", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
+]
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_PKG, "librs.so")
+
+RS_OK = 0
+RS_ERR_INVALID_VALUE = 1
+RS_ERR_UNSUPPORTED_SIZE = 2
+RS_ERR_TEMP_TOO_SMALL = 3
+RS_ERR_OVERLAP = 4
+RS_ERR_MISALIGNED = 5
+RS_ERR_HIP = 6
+
+RS_KERNEL_UPSWEEP = 0
+RS_KERNEL_ONESWEEP = 1
+RS_KERNEL_SORT_INIT = 2
+RS_KERNEL_COMPACT_INIT = 3
+RS_KERNEL_COMPACT = 4
+RS_KERNEL_BITONIC = 5
+RS_KERNEL_COPY = 6
+KERNEL_NAMES = {0: "upsweep", 1: "onesweep", 2: "sort_init", 3: "compact_init",
+                4: "compact", 5: "bitonic", 6: "copy"}
+
+EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32",
+                    "rs_compact_positive_f32", "rs_bitonic_tile", "rs_status_string",
+                    "rs_timing_enable", "rs_timing_collect"]
+
+_lib = None
+
+
+class RsError(RuntimeError):
+    def __init__(self, status, what):
+        self.status = status
+        super().__init__("%s: %s" % (what, rs_status_string(status)))
+
+
+def library_path():
+    return _LIB_PATH
+
+
+def _load():
+    global _lib
+    if _lib is not None:
+        return _lib
+    if not os.path.exists(_LIB_PATH):
+        raise RuntimeError("librs.so is not built (%s); run "
+                           "`python -m sorting_lsd_radix_amd.build` or "
+                           "`python -c 'import __graft_entry__ as g; g.build()'`" % _LIB_PATH)
+    lib = ctypes.CDLL(_LIB_PATH)
+    vp, u64, i32, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32
+    szp = ctypes.POINTER(ctypes.c_size_t)
+    lib.rs_sort_keys_u32.argtypes = [vp, vp, u64, i32, i32, vp, szp, vp]
+    lib.rs_sort_pairs_u32.argtypes = [vp, vp, vp, vp, u64, i32, i32, vp, szp, vp]
+    lib.rs_sort_pairs_f32.argtypes = [vp, vp, vp, vp, u64, i32, i32, vp, szp, vp]
+    lib.rs_compact_positive_f32.argtypes = [vp, vp, vp, u64, vp, szp, vp]
+    lib.rs_bitonic_tile.argtypes = [vp, vp, u64, u32, i32, i32, vp]
+    for f in (lib.rs_sort_keys_u32, lib.rs_sort_pairs_u32, lib.rs_sort_pairs_f32,
+              lib.rs_compact_positive_f32, lib.rs_bitonic_tile):
+        f.restype = i32
+    lib.rs_status_string.argtypes = [i32]
+    lib.rs_status_string.restype = ctypes.c_char_p
+    lib.rs_timing_enable.argtypes = [i32]
+    lib.rs_timing_enable.restype = i32
+    lib.rs_timing_collect.argtypes = [ctypes.POINTER(ctypes.c_int), ctypes.POINTER(ctypes.c_float),
+                                      i32]
+    lib.rs_timing_collect.restype = i32
+    _lib = lib
+    return lib
+
+
+# --- argument marshalling ------------------------------------------------------------
+
+def _ptr(x):
+    """Device pointer of a tensor, or an integer address, or None."""
+    if x is None:
+        return None
+    if isinstance(x, int):
+        return x
+    return x.data_ptr()
+
+
+def _stream(stream):
+    if stream is None:
+        import torch
+        return torch.cuda.current_stream().cuda_stream
+    if isinstance(stream, int):
+        return stream
+    return stream.cuda_stream
+
+
+def _call(what, status):
+    if status != RS_OK:
+        raise RsError(status, what)
+
+
+def rs_status_string(status):
+    return _load().rs_status_string(int(status)).decode()
+
+
+def _sort_call(fn, what, args, n, begin_bit, end_bit, d_temp, temp_bytes, stream):
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = fn(*[_ptr(a) for a in args], int(n), int(begin_bit), int(end_bit), _ptr(d_temp),
+            ctypes.byref(size), _stream(stream) if d_temp is not None else None)
+    _call(what, st)
+    return size.value if d_temp is None else None
+
+
+def rs_sort_keys_u32(keys_in, keys_out, n, begin_bit, end_bit, d_temp, temp_bytes, stream=None):
+    """C: rs_sort_keys_u32.  With d_temp None, returns the temp size."""
+    return _sort_call(_load().rs_sort_keys_u32, "rs_sort_keys_u32", (keys_in, keys_out), n,
+                      begin_bit, end_bit, d_temp, temp_bytes, stream)
+
+
+def rs_sort_pairs_u32(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, d_temp,
+                      temp_bytes, stream=None):
+    """C: rs_sort_pairs_u32.  With d_temp None, returns the temp size."""
+    return _sort_call(_load().rs_sort_pairs_u32, "rs_sort_pairs_u32",
+                      (keys_in, keys_out, vals_in, vals_out), n, begin_bit, end_bit, d_temp,
+                      temp_bytes, stream)
+
+
+def rs_sort_pairs_f32(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, d_temp,
+                      temp_bytes, stream=None):
+    """C: rs_sort_pairs_f32.  With d_temp None, returns the temp size."""
+    return _sort_call(_load().rs_sort_pairs_f32, "rs_sort_pairs_f32",
+                      (keys_in, keys_out, vals_in, vals_out), n, begin_bit, end_bit, d_temp,
+                      temp_bytes, stream)
+
+
+def rs_compact_positive_f32(x_in, x_out, d_count, n, d_temp, temp_bytes, stream=None):
+    """C: rs_compact_positive_f32.  With d_temp None, returns the temp size."""
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = _load().rs_compact_positive_f32(_ptr(x_in), _ptr(x_out), _ptr(d_count), int(n),
+                                         _ptr(d_temp), ctypes.byref(size),
+                                         _stream(stream) if d_temp is not None else None)
+    _call("rs_compact_positive_f32", st)
+    return size.value if d_temp is None else None
+
+
+def rs_bitonic_tile(keys_in, keys_out, n, tile, begin_bit, end_bit, stream=None):
+    """C: rs_bitonic_tile."""
+    st = _load().rs_bitonic_tile(_ptr(keys_in), _ptr(keys_out), int(n), int(tile),
+                                 int(begin_bit), int(end_bit), _stream(stream))
+    _call("rs_bitonic_tile", st)
+
+
+def rs_timing_enable(enable):
+    _call("rs_timing_enable", _load().rs_timing_enable(1 if enable else 0))
+
+
+def rs_timing_collect():
+    """[(kernel name, milliseconds), ...] of the launches recorded so far."""
+    lib = _load()
+    held = lib.rs_timing_collect(None, None, 0)
+    if held < 0:
+        raise RsError(RS_ERR_HIP, "rs_timing_collect")
+    ids = (ctypes.c_int * max(held, 1))()
+    ms = (ctypes.c_float * max(held, 1))()
+    got = lib.rs_timing_collect(ids, ms, held)
+    if got < 0:
+        raise RsError(RS_ERR_HIP, "rs_timing_collect")
+    return [(KERNEL_NAMES.get(ids[i], str(ids[i])), float(ms[i])) for i in range(min(got, held))]
+
+
+# --- convenience wrappers (torch allocates; the library computes) -------------------
+
+def _temp(nbytes, device):
+    import torch
+    return torch.empty(max(int(nbytes), 1), dtype=torch.uint8, device=device)
+
+
+def _check_tensor(t, dtype, name):
+    if not t.is_cuda or t.dtype != dtype or not t.is_contiguous():
+        raise TypeError("%s must be a contiguous CUDA tensor of %s" % (name, dtype))
+
+
+def sort_keys_u32(keys, begin_bit=0, end_bit=32, out=None, temp=None, stream=None):
+    """Stable sort of a uint32 tensor by bits [begin_bit, end_bit); returns the sorted keys."""
+    import torch
+    _check_tensor(keys, torch.uint32, "keys")
+    n = keys.numel()
+    out = torch.empty_like(keys) if out is None else out
+    need = rs_sort_keys_u32(None, None, n, begin_bit, end_bit, None, 0)
+    temp = _temp(need, keys.device) if temp is None else temp
+    rs_sort_keys_u32(keys, out, n, begin_bit, end_bit, temp, temp.numel(), stream)
+    return out
+
+
+def sort_pairs_u32(keys, vals, begin_bit=0, end_bit=32, keys_out=None, vals_out=None, temp=None,
+                   stream=None):
+    """Stable sort of uint32 (key, value) tensors; returns (keys_out, vals_out)."""
+    import torch
+    _check_tensor(keys, torch.uint32, "keys")
+    _check_tensor(vals, torch.uint32, "vals")
+    n = keys.numel()
+    keys_out = torch.empty_like(keys) if keys_out is None else keys_out
+    vals_out = torch.empty_like(vals) if vals_out is None else vals_out
+    need = rs_sort_pairs_u32(None, None, None, None, n, begin_bit, end_bit, None, 0)
+    temp = _temp(need, keys.device) if temp is None else temp
+    rs_sort_pairs_u32(keys, keys_out, vals, vals_out, n, begin_bit, end_bit, temp, temp.numel(),
+                      stream)
+    return keys_out, vals_out
+
+
+def sort_pairs_f32(keys, vals, begin_bit=0, end_bit=32, keys_out=None, vals_out=None, temp=None,
+                   stream=None):
+    """Stable IEEE-total-order sort of float32 keys with uint32 values."""
+    import torch
+    _check_tensor(keys, torch.float32, "keys")
+    _check_tensor(vals, torch.uint32, "vals")
+    n = keys.numel()
+    keys_out = torch.empty_like(keys) if keys_out is None else keys_out
+    vals_out = torch.empty_like(vals) if vals_out is None else vals_out
+    need = rs_sort_pairs_f32(None, None, None, None, n, begin_bit, end_bit, None, 0)
+    temp = _temp(need, keys.device) if temp is None else temp
+    rs_sort_pairs_f32(keys, keys_out, vals, vals_out, n, begin_bit, end_bit, temp, temp.numel(),
+                      stream)
+    return keys_out, vals_out
+
+
+def compact_positive_f32(x, out=None, count=None, temp=None, stream=None):
+    """(out, count): x > 0 kept in order at the front, +0.0 after; count is a 1-element tensor."""
+    import torch
+    _check_tensor(x, torch.float32, "x")
+    n = x.numel()
+    out = torch.empty_like(x) if out is None else out
+    count = torch.empty(1, dtype=torch.uint32, device=x.device) if count is None else count
+    need = rs_compact_positive_f32(None, None, None, n, None, 0)
+    temp = _temp(need, x.device) if temp is None else temp
+    rs_compact_positive_f32(x, out, count, n, temp, temp.numel(), stream)
+    return out, count
+
+
+def bitonic_tile(keys, tile, begin_bit=0, end_bit=32, out=None, stream=None):
+    """Each run of `tile` (<= 1024) keys sorted on its own, stably."""
+    import torch
+    _check_tensor(keys, torch.uint32, "keys")
+    out = torch.empty_like(keys) if out is None else out
+    rs_bitonic_tile(keys, out, keys.numel(), tile, begin_bit, end_bit, stream)
+    return out

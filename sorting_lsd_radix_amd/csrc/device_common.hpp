@@ -1,0 +1,70 @@
+// device_common.hpp -- wave64 and memory-scope helpers shared by the gfx950
+// kernels of the radix sort, the compaction and the bitonic tile.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace rs {
+
+constexpr int kWave = 64;          // CDNA wavefront width
+constexpr int kRadixBits = 8;      // digit width of every sort pass
+constexpr int kRadix = 1 << kRadixBits;
+
+// Cross-tile state word: 2 status bits over a 30-bit count.
+constexpr uint32_t kStateCountMask = 0x3FFFFFFFu;
+constexpr uint32_t kStateAggregate = 1u << 30;   // the tile's own count is ready
+constexpr uint32_t kStatePrefix = 2u << 30;      // the inclusive prefix is ready
+
+__device__ __forceinline__ uint32_t lane_id() {
+    return __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+}
+
+// Number of set bits of `mask` in lanes below the calling lane.
+__device__ __forceinline__ uint32_t count_below(uint64_t mask) {
+    return __builtin_amdgcn_mbcnt_hi(static_cast<uint32_t>(mask >> 32),
+                                     __builtin_amdgcn_mbcnt_lo(static_cast<uint32_t>(mask), 0u));
+}
+
+__device__ __forceinline__ uint64_t ballot(bool p) {
+    return __ballot(p);
+}
+
+// Loads/stores of tile states at device (agent) scope, so that tiles running
+// on different XCDs, each behind its own L2, see each other's words.
+__device__ __forceinline__ uint32_t load_state(const uint32_t* p) {
+    return __hip_atomic_load(p, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ void store_state(uint32_t* p, uint32_t v) {
+    __hip_atomic_store(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+__device__ __forceinline__ uint32_t fetch_add_agent(uint32_t* p, uint32_t v) {
+    return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Order-preserving transform of binary32 patterns: flips every bit of a
+// negative pattern and only the sign bit of a non-negative one.
+__device__ __forceinline__ uint32_t float_to_sortable(uint32_t u) {
+    uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u;
+    return u ^ m;
+}
+
+__device__ __forceinline__ uint32_t sortable_to_float(uint32_t s) {
+    uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(~s) >> 31) | 0x80000000u;
+    return s ^ m;
+}
+
+// Inclusive sum over the 64 lanes of a wave.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+    const uint32_t lane = lane_id();
+#pragma unroll
+    for (int off = 1; off < kWave; off <<= 1) {
+        uint32_t y = __shfl_up(x, off, kWave);
+        if (lane >= static_cast<uint32_t>(off)) x += y;
+    }
+    return x;
+}
+
+}  // namespace rs

@@ -1,0 +1,229 @@
+// rs_api.cpp -- the C ABI declared in include/rs.h: argument checks, temp
+// sizing and dispatch to the kernel launchers.  Every check runs on the host
+// before anything is enqueued, so an error return means nothing was launched.
+#include <hip/hip_runtime_api.h>
+
+#include <mutex>
+#include <vector>
+
+#include "internal.hpp"
+#include "rs.h"
+
+namespace rs {
+
+namespace {
+
+constexpr int kMaxPasses = 4;
+
+struct Range {
+    uintptr_t lo, hi;
+};
+
+Range range_of(const void* p, size_t bytes) {
+    const uintptr_t lo = reinterpret_cast<uintptr_t>(p);
+    return Range{lo, lo + bytes};
+}
+
+bool overlaps(const std::vector<Range>& rs) {
+    for (size_t i = 0; i < rs.size(); ++i)
+        for (size_t j = i + 1; j < rs.size(); ++j)
+            if (rs[i].lo < rs[i].hi && rs[j].lo < rs[j].hi && rs[i].lo < rs[j].hi &&
+                rs[j].lo < rs[i].hi)
+                return true;
+    return false;
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+bool bad_bits(int begin_bit, int end_bit) {
+    return begin_bit < 0 || end_bit > 32 || begin_bit > end_bit;
+}
+
+// ---- measurement hook ------------------------------------------------------------
+struct TimingRecord {
+    int id;
+    hipEvent_t start, stop;
+};
+
+std::mutex g_timing_mutex;
+bool g_timing_enabled = false;
+std::vector<TimingRecord> g_timing;
+
+void clear_timing_locked() {
+    for (auto& r : g_timing) {
+        (void)hipEventDestroy(r.start);
+        (void)hipEventDestroy(r.stop);
+    }
+    g_timing.clear();
+}
+
+rs_status sort_common(const uint32_t* keys_in, uint32_t* keys_out, const uint32_t* vals_in,
+                      uint32_t* vals_out, uint64_t n, int begin_bit, int end_bit, void* d_temp,
+                      size_t* temp_bytes, hipStream_t stream, bool pairs, bool is_f32) {
+    if (temp_bytes == nullptr) return RS_ERR_INVALID_VALUE;
+    if (bad_bits(begin_bit, end_bit)) return RS_ERR_INVALID_VALUE;
+    if (n >= RS_MAX_N) return RS_ERR_UNSUPPORTED_SIZE;
+    const size_t need = sort_temp_bytes(n, pairs, kMaxPasses);
+    if (d_temp == nullptr) {
+        *temp_bytes = need;
+        return RS_OK;
+    }
+    if (n == 0) return RS_OK;
+    if (keys_in == nullptr || keys_out == nullptr) return RS_ERR_INVALID_VALUE;
+    if (pairs && (vals_in == nullptr || vals_out == nullptr)) return RS_ERR_INVALID_VALUE;
+    if (!aligned16(keys_in) || !aligned16(keys_out) || !aligned16(d_temp))
+        return RS_ERR_MISALIGNED;
+    if (pairs && (!aligned16(vals_in) || !aligned16(vals_out))) return RS_ERR_MISALIGNED;
+    if (*temp_bytes < need) return RS_ERR_TEMP_TOO_SMALL;
+    std::vector<Range> rs{range_of(keys_in, n * 4), range_of(keys_out, n * 4),
+                          range_of(d_temp, need)};
+    if (pairs) {
+        rs.push_back(range_of(vals_in, n * 4));
+        rs.push_back(range_of(vals_out, n * 4));
+    }
+    if (overlaps(rs)) return RS_ERR_OVERLAP;
+
+    hipError_t e;
+    if (begin_bit == end_bit) {
+        // an empty ordering field: every key compares equal, the stable
+        // order is the input order
+        timing_before(stream, RS_KERNEL_COPY);
+        e = hipMemcpyAsync(keys_out, keys_in, n * 4, hipMemcpyDeviceToDevice, stream);
+        if (e == hipSuccess && pairs)
+            e = hipMemcpyAsync(vals_out, vals_in, n * 4, hipMemcpyDeviceToDevice, stream);
+        timing_after(stream);
+    } else {
+        e = launch_sort(keys_in, keys_out, pairs ? vals_in : nullptr, pairs ? vals_out : nullptr,
+                        static_cast<uint32_t>(n), begin_bit, end_bit, is_f32, d_temp, stream);
+    }
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+}  // namespace
+
+void timing_before(hipStream_t s, int kernel_id) {
+    std::lock_guard<std::mutex> lock(g_timing_mutex);
+    if (!g_timing_enabled) return;
+    TimingRecord r{kernel_id, nullptr, nullptr};
+    if (hipEventCreate(&r.start) != hipSuccess) return;
+    if (hipEventCreate(&r.stop) != hipSuccess) {
+        (void)hipEventDestroy(r.start);
+        return;
+    }
+    (void)hipEventRecord(r.start, s);
+    g_timing.push_back(r);
+}
+
+void timing_after(hipStream_t s) {
+    std::lock_guard<std::mutex> lock(g_timing_mutex);
+    if (!g_timing_enabled || g_timing.empty()) return;
+    (void)hipEventRecord(g_timing.back().stop, s);
+}
+
+}  // namespace rs
+
+extern "C" {
+
+rs_status rs_sort_keys_u32(const uint32_t* keys_in, uint32_t* keys_out, uint64_t n, int begin_bit,
+                           int end_bit, void* d_temp, size_t* temp_bytes, hipStream_t stream) {
+    return rs::sort_common(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, d_temp,
+                           temp_bytes, stream, false, false);
+}
+
+rs_status rs_sort_pairs_u32(const uint32_t* keys_in, uint32_t* keys_out, const uint32_t* vals_in,
+                            uint32_t* vals_out, uint64_t n, int begin_bit, int end_bit,
+                            void* d_temp, size_t* temp_bytes, hipStream_t stream) {
+    return rs::sort_common(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, d_temp,
+                           temp_bytes, stream, true, false);
+}
+
+rs_status rs_sort_pairs_f32(const float* keys_in, float* keys_out, const uint32_t* vals_in,
+                            uint32_t* vals_out, uint64_t n, int begin_bit, int end_bit,
+                            void* d_temp, size_t* temp_bytes, hipStream_t stream) {
+    return rs::sort_common(reinterpret_cast<const uint32_t*>(keys_in),
+                           reinterpret_cast<uint32_t*>(keys_out), vals_in, vals_out, n, begin_bit,
+                           end_bit, d_temp, temp_bytes, stream, true, true);
+}
+
+rs_status rs_compact_positive_f32(const float* in, float* out, uint32_t* d_count, uint64_t n,
+                                  void* d_temp, size_t* temp_bytes, hipStream_t stream) {
+    using namespace rs;
+    if (temp_bytes == nullptr) return RS_ERR_INVALID_VALUE;
+    if (n >= RS_MAX_N) return RS_ERR_UNSUPPORTED_SIZE;
+    const size_t need = compact_temp_bytes(n);
+    if (d_temp == nullptr) {
+        *temp_bytes = need;
+        return RS_OK;
+    }
+    if (d_count == nullptr) return RS_ERR_INVALID_VALUE;
+    if (n > 0 && (in == nullptr || out == nullptr)) return RS_ERR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(d_count) & 3u) != 0 || !aligned16(d_temp))
+        return RS_ERR_MISALIGNED;
+    if (n > 0 && (!aligned16(in) || !aligned16(out))) return RS_ERR_MISALIGNED;
+    if (*temp_bytes < need) return RS_ERR_TEMP_TOO_SMALL;
+    std::vector<Range> rs{range_of(d_count, 4), range_of(d_temp, need)};
+    if (n > 0) {
+        rs.push_back(range_of(in, n * 4));
+        rs.push_back(range_of(out, n * 4));
+    }
+    if (overlaps(rs)) return RS_ERR_OVERLAP;
+    hipError_t e;
+    if (n == 0)
+        e = launch_fill_zero(d_count, 1, stream, RS_KERNEL_COMPACT_INIT);
+    else
+        e = launch_compact(in, out, d_count, static_cast<uint32_t>(n), d_temp, stream);
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+rs_status rs_bitonic_tile(const uint32_t* keys_in, uint32_t* keys_out, uint64_t n, uint32_t tile,
+                          int begin_bit, int end_bit, hipStream_t stream) {
+    using namespace rs;
+    if (bad_bits(begin_bit, end_bit)) return RS_ERR_INVALID_VALUE;
+    if (tile < 1 || tile > 1024) return RS_ERR_INVALID_VALUE;
+    if (n >= RS_MAX_N) return RS_ERR_UNSUPPORTED_SIZE;
+    if (n == 0) return RS_OK;
+    if (keys_in == nullptr || keys_out == nullptr) return RS_ERR_INVALID_VALUE;
+    if (!aligned16(keys_in) || !aligned16(keys_out)) return RS_ERR_MISALIGNED;
+    if (overlaps({range_of(keys_in, n * 4), range_of(keys_out, n * 4)})) return RS_ERR_OVERLAP;
+    const hipError_t e = launch_bitonic(keys_in, keys_out, static_cast<uint32_t>(n), tile,
+                                        begin_bit, end_bit, stream);
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+const char* rs_status_string(rs_status status) {
+    switch (status) {
+        case RS_OK: return "RS_OK: success";
+        case RS_ERR_INVALID_VALUE: return "RS_ERR_INVALID_VALUE: invalid argument";
+        case RS_ERR_UNSUPPORTED_SIZE: return "RS_ERR_UNSUPPORTED_SIZE: n must be below 2^30";
+        case RS_ERR_TEMP_TOO_SMALL: return "RS_ERR_TEMP_TOO_SMALL: temporary buffer too small";
+        case RS_ERR_OVERLAP: return "RS_ERR_OVERLAP: buffers overlap";
+        case RS_ERR_MISALIGNED: return "RS_ERR_MISALIGNED: pointer not 16-byte aligned";
+        case RS_ERR_HIP: return "RS_ERR_HIP: HIP launch or runtime error";
+    }
+    return "unknown rs_status";
+}
+
+rs_status rs_timing_enable(int enable) {
+    std::lock_guard<std::mutex> lock(rs::g_timing_mutex);
+    if (enable) rs::clear_timing_locked();
+    rs::g_timing_enabled = enable != 0;
+    return RS_OK;
+}
+
+int rs_timing_collect(int* kernel_ids, float* ms, int cap) {
+    std::lock_guard<std::mutex> lock(rs::g_timing_mutex);
+    const int held = static_cast<int>(rs::g_timing.size());
+    for (int i = 0; i < held; ++i) {
+        const rs::TimingRecord& r = rs::g_timing[i];
+        if (hipEventSynchronize(r.stop) != hipSuccess) return -1;
+        float t = 0.f;
+        if (hipEventElapsedTime(&t, r.start, r.stop) != hipSuccess) return -1;
+        if (i < cap) {
+            if (kernel_ids) kernel_ids[i] = r.id;
+            if (ms) ms[i] = t;
+        }
+    }
+    return held;
+}
+
+}  // extern "C"
