@@ -29,12 +29,15 @@ namespace rs {
 
 namespace {
 
-constexpr int kSortBlock = 512;
+constexpr int kSortBlock = 1024;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
+constexpr int kSortLookback = 8;       // earlier tiles read per look-back batch
+constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
+constexpr int kGroups = 8;             // XCDs
 
 constexpr int kUpBlock = 256;
-constexpr int kUpSub = 4;          // sub-histograms per digit (spreads LDS atomics)
+constexpr int kUpSub = 8;          // sub-histograms per digit (spreads LDS atomics)
 constexpr int kMaxPasses = 4;
 
 constexpr size_t kAlign = 256;
@@ -63,6 +66,7 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 struct PassDigits {
     uint32_t shift[kMaxPasses];
     uint32_t mask[kMaxPasses];
+    uint32_t width[kMaxPasses];
     uint32_t passes;
 };
 
@@ -91,7 +95,21 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
     const uint32_t nvec = n / 4;
     const uint4* k4 = reinterpret_cast<const uint4*>(keys);
     const uint32_t stride = gridDim.x * kUpBlock;
-    for (uint32_t i = blockIdx.x * kUpBlock + threadIdx.x; i < nvec; i += stride) {
+    uint32_t i = blockIdx.x * kUpBlock + threadIdx.x;
+    // four 16-byte loads in flight per thread before the LDS counting
+    for (; i + 3 * stride < nvec; i += 4 * stride) {
+        uint4 q[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) q[u] = k4[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            count_key<FLIP>(s_hist, q[u].x, pd, sub);
+            count_key<FLIP>(s_hist, q[u].y, pd, sub);
+            count_key<FLIP>(s_hist, q[u].z, pd, sub);
+            count_key<FLIP>(s_hist, q[u].w, pd, sub);
+        }
+    }
+    for (; i < nvec; i += stride) {
         const uint4 q = k4[i];
         count_key<FLIP>(s_hist, q.x, pd, sub);
         count_key<FLIP>(s_hist, q.y, pd, sub);
@@ -114,31 +132,106 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
 // One-sweep pass: stable scatter of one 8-bit digit.
 // ---------------------------------------------------------------------------
 
-// Lanes of the wave whose digit equals this lane's (eight ballots).
-__device__ __forceinline__ uint64_t lanes_with_same_digit(uint32_t d) {
-    uint64_t peers = ~0ull;
+// Lanes of the wave whose digit differs from this lane's (eight ballots).  For
+// each bit, m is 0 or all ones (the bit sign-extended) and the ballot marks
+// the lanes whose bit is set; lanes that differ from this one in that bit are
+// vote ^ m.  The sets are OR-ed with one 3-input logic op per half (truth
+// table A | (B ^ C) = 0xF6 in the A=0xF0, B=0xCC, C=0xAA convention).  The
+// ballot is taken from m itself (one compare) through a small asm statement,
+// which keeps the compiler from re-deriving the bit with a shift first.
+__device__ __forceinline__ uint64_t lanes_with_other_digit(uint32_t d) {
+    uint32_t diff_lo = 0u, diff_hi = 0u;
 #pragma unroll
     for (int b = 0; b < kRadixBits; ++b) {
-        const bool bit = (d >> b) & 1u;
-        const uint64_t vote = ballot(bit);
-        peers &= bit ? vote : ~vote;
+        const uint32_t m = static_cast<uint32_t>(__builtin_amdgcn_sbfe(static_cast<int>(d), b, 1));
+        uint64_t vote;
+        asm volatile("v_cmp_ne_u32_e64 %0, 0, %1" : "=s"(vote) : "v"(m));
+        diff_lo = __builtin_amdgcn_bitop3_b32(diff_lo, static_cast<uint32_t>(vote), m, 0xF6);
+        diff_hi = __builtin_amdgcn_bitop3_b32(diff_hi, static_cast<uint32_t>(vote >> 32), m, 0xF6);
     }
-    return peers;
+    return (static_cast<uint64_t>(diff_hi) << 32) | diff_lo;
 }
 
-template <int BLOCK, int ITEMS, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
-__global__ __launch_bounds__(BLOCK) void onesweep_kernel(
-    const uint32_t* __restrict__ src_keys, uint32_t* __restrict__ dst_keys,
-    const uint32_t* __restrict__ src_vals, uint32_t* __restrict__ dst_vals, uint32_t n,
-    uint32_t shift, uint32_t mask, const uint32_t* __restrict__ bins,
-    uint32_t* __restrict__ states, uint32_t* __restrict__ next_states,
-    uint32_t* __restrict__ tile_counter) {
+// Arguments of one digit pass.
+struct PassArgs {
+    const uint32_t* src_keys;
+    uint32_t* dst_keys;
+    const uint32_t* src_vals;
+    uint32_t* dst_vals;
+    uint32_t n, tiles, shift, width;   // digit = bits [shift, shift + width) of the key
+    const uint32_t* bins;      // global digit counts of this pass
+    uint32_t* states;          // look-back words of this pass, zeroed
+    uint32_t* next_states;     // look-back words of the next pass, cleared here (or null)
+    uint32_t* sched;           // tile scheduler of this pass, zeroed
+    uint32_t max_chunks;       // chunk-map entries per XCD group
+};
+
+// Index of the XCD (accelerator complex die) this wave runs on.
+__device__ __forceinline__ uint32_t xcd_id() {
+    return static_cast<uint32_t>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20)) & 0xFu;
+}
+
+// Tile scheduler.  Tiles are handed out in chunks of kChunk consecutive tiles;
+// each XCD group works through one chunk at a time, so neighbouring tiles run
+// on the same XCD and the cache lines their digit runs share are merged in
+// that XCD's L2 before they reach memory.  Chunks are taken from one global
+// counter in order, and a group takes the tiles of its chunk in order.  The
+// tile with the smallest index among the running ones therefore has every
+// earlier tile either finished or running, so look-back always makes progress.
+// Layout: sched[0] global chunk counter, sched[1 + g] tiles taken by group g,
+// sched[16 + g * max_chunks + j] = 1 + global index of group g's j-th chunk.
+__device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t max_chunks, uint32_t group,
+                                              uint32_t tiles) {
+    const uint32_t k = fetch_add_agent(&sched[1 + group], 1u);
+    const uint32_t j = k / kChunk, off = k % kChunk;
+    if (j >= max_chunks) return tiles;   // never reached: max_chunks covers every taker
+    uint32_t* slot = &sched[16 + group * max_chunks + j];
+    uint32_t c;
+    if (off == 0) {
+        c = fetch_add_agent(&sched[0], 1u);
+        store_state(slot, c + 1u);
+    } else {
+        uint32_t v;
+        while ((v = load_state(slot)) == 0u) __builtin_amdgcn_s_sleep(1);
+        c = v - 1u;
+    }
+    const uint64_t t = static_cast<uint64_t>(c) * kChunk + off;
+    return t < tiles ? static_cast<uint32_t>(t) : tiles;
+}
+
+// Loads the ITEMS keys of this lane for `tile`: row j of wave w is the 64
+// consecutive keys at tile*TILE + w*64*ITEMS + j*64.  Partial tiles read only
+// in-range addresses (clamped); the padding is applied after the flip.
+template <int ITEMS, int TILE>
+__device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint32_t tile,
+                                          uint32_t n, uint32_t wave, uint32_t lane,
+                                          uint32_t (&x)[ITEMS]) {
+    const uint32_t first = tile * TILE + wave * (kWave * ITEMS) + lane;
+    if (tile * TILE + TILE <= n) {
+        const uint32_t* p = src + first;   // row offsets fold into the load instruction
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) x[j] = p[j * kWave];
+    } else {
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t idx = first + j * kWave;
+            x[j] = src[idx < n ? idx : n - 1];
+        }
+    }
+}
+
+// One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
+// tiles the scheduler hands it.
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
+__global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
+    static_assert((TILE & (TILE - 1)) == 0, "tile must be a power of two");
+    static_assert(ITEMS % 4 == 0, "digits are packed four per register");
 
-    __shared__ uint32_t s_keys[TILE];
-    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    // One staging buffer: the keys in digit order, then the values in digit order.
+    __shared__ uint32_t s_buf[TILE];
     __shared__ uint32_t s_off[WAVES * kRadix];   // per-wave digit counters, then offsets
     __shared__ uint32_t s_adjust[kRadix];
     __shared__ uint32_t s_wsum[2][kRadix / kWave];
@@ -147,168 +240,242 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t wave = tid / kWave;
+    const uint32_t* __restrict__ src_keys = a.src_keys;
+    uint32_t* __restrict__ dst_keys = a.dst_keys;
+    const uint32_t* __restrict__ src_vals = a.src_vals;
+    uint32_t* __restrict__ dst_vals = a.dst_vals;
+    uint32_t* __restrict__ states = a.states;
+    const uint32_t n = a.n, shift = a.shift, width = a.width, tiles = a.tiles;
+    const uint32_t last_digit = (1u << width) - 1u;
+    const uint32_t group = xcd_id() % kGroups;
 
-    if (tid == 0) s_tile = fetch_add_agent(tile_counter, 1u);
-    for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
     // global digit count of this pass (thread d holds digit d)
-    const uint32_t bin = (tid < kRadix) ? bins[tid] : 0u;
-    __syncthreads();
+    const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
 
-    const uint32_t tile = s_tile;
-    const uint32_t tile_base = tile * TILE;
-    const uint32_t valid = (n - tile_base < static_cast<uint32_t>(TILE)) ? n - tile_base : TILE;
-    const bool full = (valid == static_cast<uint32_t>(TILE));
+    for (;;) {
+        // The tile is taken only when the block can start on it at once, so
+        // its count is published as early as possible.
+        if (tid == 0) s_tile = next_tile(a.sched, a.max_chunks, group, tiles);
+        for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
+        __syncthreads();
+        const uint32_t tile = s_tile;
+        if (tile >= tiles) break;   // uniform: no tiles left
+        uint32_t k[ITEMS];
+        load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
+        const uint32_t tile_base = tile * TILE;
+        const uint32_t valid = (n - tile_base < static_cast<uint32_t>(TILE)) ? n - tile_base : TILE;
+        const bool full = (valid == static_cast<uint32_t>(TILE));
+        const uint32_t first = tile_base + wave * (kWave * ITEMS) + lane;
+        if (FLIP_IN) {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) k[j] = float_to_sortable(k[j]);
+        }
+        if (!full) {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j)
+                if (first + j * kWave >= n) k[j] = 0xFFFFFFFFu;   // padding sorts last
+        }
 
-    // ---- load: row j of wave w is 64 consecutive keys -------------------------
-    uint32_t k[ITEMS];
-    uint32_t v[PAIRS ? ITEMS : 1];
-    const uint32_t first = tile_base + wave * (kWave * ITEMS) + lane;
-    if (full) {
+        // ---- stable rank inside the wave --------------------------------------
+        uint32_t pos[ITEMS];   // rank in the wave, later the position in the tile
+        uint32_t* my_count = s_off + wave * kRadix;
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            k[j] = src_keys[first + j * kWave];
-            if (PAIRS) v[j] = src_vals[first + j * kWave];
+            const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+            const uint64_t others = lanes_with_other_digit(d);
+            const uint32_t below = lane - count_below(others);      // same digit, lower lane
+            const uint32_t before = my_count[d];
+            if (below == 0)
+                my_count[d] = before + kWave - static_cast<uint32_t>(__popcll(others));
+            pos[j] = before + below;
+            // the slots are chained through the LDS counters anyway; keeping the
+            // scheduler from interleaving them keeps register pressure low
+            __builtin_amdgcn_sched_barrier(0);
         }
-    } else {
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t idx = first + j * kWave;
-            const bool in = idx < n;
-            k[j] = in ? src_keys[idx] : 0u;
-            if (PAIRS) v[j] = in ? src_vals[idx] : 0u;
-        }
-    }
-#pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        if (FLIP_IN) k[j] = float_to_sortable(k[j]);
-        if (!full && first + j * kWave >= n) k[j] = 0xFFFFFFFFu;   // padding sorts last
-    }
+        __syncthreads();
 
-    // ---- stable rank inside the wave ------------------------------------------
-    uint32_t rank[ITEMS];
-    uint32_t* my_count = s_off + wave * kRadix;
+        // ---- per digit: offsets of each wave, tile count, scans -------------
+        uint32_t count = 0;
+        if (tid < kRadix) {
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const uint32_t d = (k[j] >> shift) & mask;
-        const uint64_t peers = lanes_with_same_digit(d);
-        const uint32_t below = count_below(peers);
-        const uint32_t before = my_count[d];
-        if (below == 0) my_count[d] = before + static_cast<uint32_t>(__popcll(peers));
-        rank[j] = before + below;
-    }
-    __syncthreads();
-
-    // ---- per digit: offsets of each wave, tile count, scans -----------------
-    uint32_t count = 0;
-    if (tid < kRadix) {
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) {
-            const uint32_t c = s_off[w * kRadix + tid];
-            s_off[w * kRadix + tid] = count;
-            count += c;
-        }
-    }
-    // the padding of a partial tile sits in the last digit; it is not published
-    const uint32_t pads = full ? 0u : static_cast<uint32_t>(TILE) - valid;
-    const uint32_t real = (tid == mask) ? count - pads : count;
-    if (tid < kRadix)
-        store_state(&states[tile * kRadix + tid], (tile == 0 ? kStatePrefix : kStateAggregate) | real);
-
-    uint32_t inc_c = 0, inc_b = 0;
-    if (tid < kRadix) {
-        inc_c = wave_inclusive_sum(count);
-        inc_b = wave_inclusive_sum(bin);
-        if (lane == kWave - 1) {
-            s_wsum[0][wave] = inc_c;
-            s_wsum[1][wave] = inc_b;
-        }
-    }
-    __syncthreads();
-    uint32_t local_start = 0, bin_start = 0;
-    if (tid < kRadix) {
-        uint32_t pc = 0, pb = 0;
-#pragma unroll
-        for (int w = 0; w < kRadix / kWave; ++w) {
-            if (w < static_cast<int>(wave)) {
-                pc += s_wsum[0][w];
-                pb += s_wsum[1][w];
+            for (int w = 0; w < WAVES; ++w) {
+                const uint32_t c = s_off[w * kRadix + tid];
+                s_off[w * kRadix + tid] = count;
+                count += c;
             }
         }
-        local_start = pc + inc_c - count;
-        bin_start = pb + inc_b - bin;
-#pragma unroll
-        for (int w = 0; w < WAVES; ++w) s_off[w * kRadix + tid] += local_start;
-    }
-    __syncthreads();
+        // the padding of a partial tile sits in the last digit; it is not published
+        const uint32_t pads = full ? 0u : static_cast<uint32_t>(TILE) - valid;
+        const uint32_t real = (tid == last_digit) ? count - pads : count;
+        if (tid < kRadix)
+            store_state(&states[tile * kRadix + tid],
+                        (tile == 0 ? kStatePrefix : kStateAggregate) | real);
 
-    // ---- re-lay the tile out in digit order in LDS -------------------------------
+        uint32_t inc_c = 0, inc_b = 0;
+        if (tid < kRadix) {
+            inc_c = wave_inclusive_sum(count);
+            inc_b = wave_inclusive_sum(bin);
+            if (lane == kWave - 1) {
+                s_wsum[0][wave] = inc_c;
+                s_wsum[1][wave] = inc_b;
+            }
+        }
+        __syncthreads();
+        uint32_t local_start = 0, bin_start = 0;
+        if (tid < kRadix) {
+            uint32_t pc = 0, pb = 0;
 #pragma unroll
-    for (int j = 0; j < ITEMS; ++j) {
-        const uint32_t d = (k[j] >> shift) & mask;
-        const uint32_t pos = s_off[wave * kRadix + d] + rank[j];
-        s_keys[pos] = k[j];
-        if (PAIRS) s_vals[pos] = v[j];
-    }
-
-    // ---- decoupled look-back: same-digit keys in all earlier tiles ------------
-    if (tid < kRadix) {
-        uint32_t excl = 0;
-        if (tile > 0) {
-            int32_t t = static_cast<int32_t>(tile) - 1;
-            for (;;) {
-                const uint32_t s = load_state(&states[static_cast<uint32_t>(t) * kRadix + tid]);
-                if ((s & ~kStateCountMask) == 0u) {
-                    __builtin_amdgcn_s_sleep(1);
-                    continue;
+            for (int w = 0; w < kRadix / kWave; ++w) {
+                if (w < static_cast<int>(wave)) {
+                    pc += s_wsum[0][w];
+                    pb += s_wsum[1][w];
                 }
-                excl += s & kStateCountMask;
-                if (s & kStatePrefix) break;
-                --t;
             }
-            store_state(&states[tile * kRadix + tid], kStatePrefix | (excl + real));
-        }
-        s_adjust[tid] = bin_start + excl - local_start;
-        if (next_states) next_states[tile * kRadix + tid] = 0u;
-    }
-    __syncthreads();
-
-    // ---- scatter each digit run to consecutive addresses --------------------------
+            local_start = pc + inc_c - count;
+            bin_start = pb + inc_b - bin;
 #pragma unroll
-    for (int r = 0; r < ITEMS; ++r) {
-        const uint32_t i = r * BLOCK + tid;
-        if (full || i < valid) {
-            const uint32_t key = s_keys[i];
-            const uint32_t dst = i + s_adjust[(key >> shift) & mask];
-            if (dst < n) {   // always true for consistent counts; guards the store
-                dst_keys[dst] = FLIP_OUT ? sortable_to_float(key) : key;
-                if (PAIRS) dst_vals[dst] = s_vals[i];
+            for (int w = 0; w < WAVES; ++w) s_off[w * kRadix + tid] += local_start;
+        }
+        __syncthreads();
+
+        // First look-back batch: the states of this digit in the LOOKBACK tiles
+        // before this one, loaded together so their latencies overlap each
+        // other and the work below.
+        uint32_t lb[LOOKBACK];
+        if (tid < kRadix && tile > 0) {
+#pragma unroll
+            for (int b = 0; b < LOOKBACK; ++b) {
+                const int32_t t = static_cast<int32_t>(tile) - 1 - b;
+                lb[b] = (t >= 0) ? load_state(&states[static_cast<uint32_t>(t) * kRadix + tid]) : 0u;
             }
         }
+
+        // The values are loaded now; their latency overlaps the re-layout of
+        // the keys and the look-back, and they do not hold registers during
+        // the rank.
+        uint32_t v[PAIRS ? ITEMS : 1];
+        if constexpr (PAIRS) load_rows<ITEMS, TILE>(src_vals, tile, n, wave, lane, v);
+
+        // ---- re-lay the keys out in digit order in LDS ---------------------------
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            // recompute the digit rather than keep the rank loop's LDS addresses
+            // alive across the scans (an empty asm hides the reuse)
+            uint32_t key = k[j];
+            asm volatile("" : "+v"(key));
+            const uint32_t d = __builtin_amdgcn_ubfe(key, shift, width);
+            // (the mask never changes a consistent position; it keeps the store in the tile)
+            pos[j] = (s_off[wave * kRadix + d] + pos[j]) & (TILE - 1);
+            s_buf[pos[j]] = key;
+        }
+
+        // ---- decoupled look-back: same-digit keys in all earlier tiles --------
+        // Walk from the nearest earlier tile down, adding published tile counts
+        // until the first published inclusive prefix; states are read in
+        // batches of LOOKBACK tiles.  Tile 0 always publishes a prefix, so the
+        // walk ends at tile 0 at the latest and never reads below it.
+        if (tid < kRadix) {
+            uint32_t excl = 0;
+            if (tile > 0) {
+                int32_t nearest = static_cast<int32_t>(tile) - 1;   // tile of lb[0]
+                bool done = false;
+                for (;;) {
+#pragma unroll
+                    for (int b = 0; b < LOOKBACK; ++b) {
+                        if (!done) {
+                            const uint32_t t = static_cast<uint32_t>(nearest - b);
+                            uint32_t st = lb[b];
+                            while ((st & ~kStateCountMask) == 0u) {
+                                __builtin_amdgcn_s_sleep(1);
+                                st = load_state(&states[t * kRadix + tid]);
+                            }
+                            excl += st & kStateCountMask;
+                            done = (st & kStatePrefix) != 0u;
+                        }
+                    }
+                    if (done) break;
+                    nearest -= LOOKBACK;
+#pragma unroll
+                    for (int b = 0; b < LOOKBACK; ++b) {
+                        const int32_t t = nearest - b;
+                        lb[b] = (t >= 0) ? load_state(&states[static_cast<uint32_t>(t) * kRadix + tid])
+                                         : 0u;
+                    }
+                }
+                store_state(&states[tile * kRadix + tid], kStatePrefix | (excl + real));
+            }
+            s_adjust[tid] = bin_start + excl - local_start;
+            if (a.next_states) a.next_states[tile * kRadix + tid] = 0u;
+        }
+        __syncthreads();
+
+        // ---- scatter each digit run to consecutive addresses ----------------------
+        // Slot r of this thread is tile position r * BLOCK + tid; its digit is
+        // kept (four per register) for the value scatter.
+        uint32_t digits[PAIRS ? ITEMS / 4 : 1];
+#pragma unroll
+        for (int r = 0; r < ITEMS; ++r) {
+            const uint32_t i = r * BLOCK + tid;
+            const uint32_t key = s_buf[i];
+            const uint32_t d = __builtin_amdgcn_ubfe(key, shift, width);
+            if (PAIRS) {
+                if (r % 4 == 0) digits[r / 4] = d;
+                else digits[r / 4] |= d << (8 * (r % 4));
+            }
+            if (full || i < valid) {
+                const uint32_t dst = i + s_adjust[d];
+                if (dst < n)   // always true for consistent counts; guards the store
+                    dst_keys[dst] = FLIP_OUT ? sortable_to_float(key) : key;
+            }
+            if (PAIRS && r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounds live registers
+        }
+        if (PAIRS) {
+            __syncthreads();   // every key has been read from the staging buffer
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) s_buf[pos[j]] = v[j];
+            __syncthreads();
+#pragma unroll
+            for (int r = 0; r < ITEMS; ++r) {
+                const uint32_t i = r * BLOCK + tid;
+                if (full || i < valid) {
+                    const uint32_t d = (digits[r / 4] >> (8 * (r % 4))) & 0xFFu;
+                    const uint32_t dst = i + s_adjust[d];
+                    if (dst < n) dst_vals[dst] = s_buf[i];
+                }
+            }
+        }
+        // the next iteration rewrites s_off and s_buf only after a barrier
     }
 }
 
 // Temp layout (every piece 256-byte aligned):
 //   bins     [kMaxPasses][256] u32   global digit counts of each pass
-//   counters [kMaxPasses]      u32   tile-id counters, padded to 256 B
+//   sched    [kMaxPasses][sched_words] u32   tile schedulers (see next_tile)
 //   states0  [tiles][256]      u32   look-back states of even passes
 //   states1  [tiles][256]      u32   look-back states of odd passes (passes >= 2)
 //   tmp_keys [n] u32, tmp_vals [n] u32   ping-pong buffers (passes >= 2)
-// bins, counters and states0 are contiguous and cleared by one fill launch.
+// bins, sched and states0 are contiguous and cleared by one fill launch.
 struct SortLayout {
-    size_t bins, counters, states0, states1, tmp_keys, tmp_vals, total;
+    size_t bins, sched, states0, states1, tmp_keys, tmp_vals, total;
     uint64_t clear_words;
-    uint32_t tiles;
+    uint32_t tiles, max_chunks, sched_words;
 };
+
+// Upper bound of the blocks one pass keeps resident (sizes the chunk map).
+constexpr uint32_t kMaxResidentBlocks = 4096;
 
 SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
     SortLayout L{};
     L.tiles = static_cast<uint32_t>((n + kSortTile - 1) / kSortTile);
+    // a group's j-th chunk exists for j <= chunks + (its blocks) / kChunk
+    L.max_chunks = (L.tiles + kChunk - 1) / kChunk + kMaxResidentBlocks / kChunk + 2;
+    L.sched_words = static_cast<uint32_t>(align_up((16 + kGroups * L.max_chunks) * 4) / 4);
     const size_t states_bytes = align_up(static_cast<size_t>(L.tiles) * kRadix * 4);
     size_t off = 0;
     L.bins = off;
     off += align_up(kMaxPasses * kRadix * 4);
-    L.counters = off;
-    off += align_up(kMaxPasses * 4);
+    L.sched = off;
+    off += static_cast<size_t>(kMaxPasses) * L.sched_words * 4;
     L.states0 = off;
     off += states_bytes;
     L.clear_words = off / 4;
@@ -322,27 +489,7 @@ SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
     return L;
 }
 
-template <int BLOCK, int ITEMS, bool PAIRS>
-hipError_t launch_pass(bool flip_in, bool flip_out, dim3 grid, hipStream_t s,
-                       const uint32_t* sk, uint32_t* dk, const uint32_t* sv, uint32_t* dv,
-                       uint32_t n, uint32_t shift, uint32_t mask, const uint32_t* bins,
-                       uint32_t* states, uint32_t* next_states, uint32_t* counter) {
-    if (flip_in && flip_out)
-        onesweep_kernel<BLOCK, ITEMS, PAIRS, true, true><<<grid, BLOCK, 0, s>>>(
-            sk, dk, sv, dv, n, shift, mask, bins, states, next_states, counter);
-    else if (flip_in)
-        onesweep_kernel<BLOCK, ITEMS, PAIRS, true, false><<<grid, BLOCK, 0, s>>>(
-            sk, dk, sv, dv, n, shift, mask, bins, states, next_states, counter);
-    else if (flip_out)
-        onesweep_kernel<BLOCK, ITEMS, PAIRS, false, true><<<grid, BLOCK, 0, s>>>(
-            sk, dk, sv, dv, n, shift, mask, bins, states, next_states, counter);
-    else
-        onesweep_kernel<BLOCK, ITEMS, PAIRS, false, false><<<grid, BLOCK, 0, s>>>(
-            sk, dk, sv, dv, n, shift, mask, bins, states, next_states, counter);
-    return hipGetLastError();
-}
-
-int upsweep_grid(uint32_t n) {
+int device_cus() {
     static int cus = 0;
     if (cus == 0) {
         int dev = 0;
@@ -351,10 +498,44 @@ int upsweep_grid(uint32_t n) {
             cus <= 0)
             cus = 256;
     }
+    return cus;
+}
+
+// Resident blocks of one pass kernel instance (occupancy x CUs), cached.
+template <typename K>
+uint32_t resident_blocks(K kernel, int block) {
+    int per_cu = 0;
+    if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kernel, block, 0) != hipSuccess ||
+        per_cu <= 0)
+        per_cu = 1;
+    uint32_t r = static_cast<uint32_t>(per_cu) * static_cast<uint32_t>(device_cus());
+    return r < kMaxResidentBlocks ? r : kMaxResidentBlocks;
+}
+
+template <int BLOCK, int ITEMS, bool PAIRS, bool FI, bool FO>
+hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
+    static uint32_t resident = 0;
+    auto kern = onesweep_kernel<BLOCK, ITEMS, kSortLookback, PAIRS, FI, FO>;
+    if (resident == 0) resident = resident_blocks(kern, BLOCK);
+    const uint32_t grid = a.tiles < resident ? a.tiles : resident;
+    kern<<<dim3(grid), BLOCK, 0, s>>>(a);
+    return hipGetLastError();
+}
+
+template <bool PAIRS>
+hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
+    if (flip_in && flip_out) return launch_pass_t<kSortBlock, kSortItems, PAIRS, true, true>(a, s);
+    if (flip_in) return launch_pass_t<kSortBlock, kSortItems, PAIRS, true, false>(a, s);
+    if (flip_out) return launch_pass_t<kSortBlock, kSortItems, PAIRS, false, true>(a, s);
+    return launch_pass_t<kSortBlock, kSortItems, PAIRS, false, false>(a, s);
+}
+
+int upsweep_grid(uint32_t n) {
+    const int cus = device_cus();
     const uint64_t vec_per_block = static_cast<uint64_t>(kUpBlock) * 16;   // >= 16 uint4 per thread
     uint64_t g = (static_cast<uint64_t>(n) / 4 + vec_per_block - 1) / vec_per_block;
     if (g < 1) g = 1;
-    if (g > static_cast<uint64_t>(cus) * 2) g = static_cast<uint64_t>(cus) * 2;
+    if (g > static_cast<uint64_t>(cus) * 4) g = static_cast<uint64_t>(cus) * 4;
     return static_cast<int>(g);
 }
 
@@ -386,7 +567,7 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
     const SortLayout L = sort_layout(n, pairs, passes);
     char* base = static_cast<char*>(temp);
     uint32_t* bins = reinterpret_cast<uint32_t*>(base + L.bins);
-    uint32_t* counters = reinterpret_cast<uint32_t*>(base + L.counters);
+    uint32_t* sched = reinterpret_cast<uint32_t*>(base + L.sched);
     uint32_t* states[2] = {reinterpret_cast<uint32_t*>(base + L.states0),
                            reinterpret_cast<uint32_t*>(base + L.states1)};
     uint32_t* tmp_keys = reinterpret_cast<uint32_t*>(base + L.tmp_keys);
@@ -403,6 +584,7 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
         const int w = (end_bit - s < kRadixBits) ? end_bit - s : kRadixBits;
         pd.shift[p] = static_cast<uint32_t>(s);
         pd.mask[p] = (1u << w) - 1u;
+        pd.width[p] = static_cast<uint32_t>(w);
     }
     timing_before(stream, RS_KERNEL_UPSWEEP);
     if (is_f32)
@@ -413,31 +595,33 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
     timing_after(stream);
     if (e != hipSuccess) return e;
 
-    const dim3 grid(L.tiles);
     const uint32_t* sk = keys_in;
     const uint32_t* sv = vals_in;
     for (int p = 0; p < passes; ++p) {
         const bool to_out = ((passes - 1 - p) % 2) == 0;
-        uint32_t* dk = to_out ? keys_out : tmp_keys;
-        uint32_t* dv = pairs ? (to_out ? vals_out : tmp_vals) : nullptr;
-        uint32_t* next = (p + 1 < passes) ? states[(p + 1) & 1] : nullptr;
+        PassArgs a{};
+        a.src_keys = sk;
+        a.dst_keys = to_out ? keys_out : tmp_keys;
+        a.src_vals = sv;
+        a.dst_vals = pairs ? (to_out ? vals_out : tmp_vals) : nullptr;
+        a.n = n;
+        a.tiles = L.tiles;
+        a.shift = pd.shift[p];
+        a.width = pd.width[p];
+        a.bins = bins + p * kRadix;
+        a.states = states[p & 1];
+        a.next_states = (p + 1 < passes) ? states[(p + 1) & 1] : nullptr;
+        a.sched = sched + static_cast<size_t>(p) * L.sched_words;
+        a.max_chunks = L.max_chunks;
         const bool flip_in = is_f32 && p == 0;
         const bool flip_out = is_f32 && p == passes - 1;
         timing_before(stream, RS_KERNEL_ONESWEEP);
-        if (pairs)
-            e = launch_pass<kSortBlock, kSortItems, true>(flip_in, flip_out, grid, stream, sk, dk, sv,
-                                                          dv, n, pd.shift[p], pd.mask[p],
-                                                          bins + p * kRadix, states[p & 1], next,
-                                                          counters + p);
-        else
-            e = launch_pass<kSortBlock, kSortItems, false>(flip_in, flip_out, grid, stream, sk, dk,
-                                                           nullptr, nullptr, n, pd.shift[p],
-                                                           pd.mask[p], bins + p * kRadix,
-                                                           states[p & 1], next, counters + p);
+        e = pairs ? launch_pass<true>(flip_in, flip_out, a, stream)
+                  : launch_pass<false>(flip_in, flip_out, a, stream);
         timing_after(stream);
         if (e != hipSuccess) return e;
-        sk = dk;
-        sv = dv;
+        sk = a.dst_keys;
+        sv = a.dst_vals;
     }
     return hipSuccess;
 }
