@@ -1,18 +1,22 @@
-"""Throughput of the stable LSD radix sort on one MI355X.
+"""Throughput of the stable LSD radix sort (and its companions) on one MI355X.
 
 Default workload: 2^28 uniform u32 keys with u32 values (original indices),
 full 32-bit keys, 4 passes of 8-bit digits.  One step = one whole
 rs_sort_pairs_u32 call (fill, upsweep histogram, 4 one-sweep passes) with
 inputs, outputs and temp already resident in HBM.  Prints one JSON line.
 
-  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME]
-                  [--no-cpu-baseline] [--copy-calibration]
+  python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
+                  [--no-cpu-baseline] [--no-check] [--copy-calibration]
 
-The roofline entry is for the dominant kernel (the one-sweep pass): its
-algorithmic bytes per launch (read + write of keys and values, 16 B per key)
-over its mean duration, timed with HIP events the library records around
-each launch on the call's stream during the timed steps.  The CPU baseline is
-the oracle (single-threaded C) on a bounded prefix of the same workload.
+The roofline entry is for the dominant kernel of the workload (the one-sweep
+pass for sorts, the compaction kernel for compaction): its algorithmic bytes
+per launch over its mean duration, timed with HIP events that the library
+records around each of its launches on the call's stream during the timed
+steps.  Algorithmic bytes: 16 B per key per pass for key-value sorts (read and
+write key and value), 8 B for keys-only sorts, 8 B per element for compaction
+(read the input, write the output including the zero tail).  The CPU baseline
+is the oracle (single-threaded C) on a bounded prefix of the same workload.
+--all prints one line per workload (the default line first).
 """
 import argparse
 import hashlib
@@ -26,64 +30,243 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 PROFILES = os.path.join(ROOT, "profiles")
-TRAFFIC_FILE = os.path.join(PROFILES, "onesweep_pairs_u32_2p28_traffic.json")
-KERNEL_SOURCE = os.path.join(ROOT, "sorting_lsd_radix_amd", "csrc", "radix.hip")
+TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
+CSRC = os.path.join(ROOT, "sorting_lsd_radix_amd", "csrc")
 
+# name: (description, kind, n, begin_bit, end_bit)
 WORKLOADS = {
-    # name: (description, n, pairs, is_f32, begin_bit, end_bit)
     "pairs_u32_2p28": ("uniform u32 key-value pairs, n=2^28, bits [0,32), 4 passes",
-                       1 << 28, True, False, 0, 32),
+                       "pairs_u32", 1 << 28, 0, 32),
     "keys_u32_2p28": ("uniform u32 keys only, n=2^28, bits [0,32), 4 passes",
-                      1 << 28, False, False, 0, 32),
+                      "keys_u32", 1 << 28, 0, 32),
     "pairs_f32_2p28": ("N(0,1) f32 keys with injected +-0 and +-1e-38, index values, n=2^28, "
-                       "4 passes", 1 << 28, True, True, 0, 32),
-    "pairs_zipf_2p26": ("Zipf(1.2) u32 keys over 65536 values, index values, n=2^26, bits [0,16), "
-                        "2 passes", 1 << 26, True, False, 0, 16),
+                       "4 passes", "pairs_f32", 1 << 28, 0, 32),
+    "pairs_zipf_2p26": ("Zipf(1.2) u32 keys over 65536 values, index values, n=2^26, "
+                        "bits [0,16), 2 passes", "pairs_u32", 1 << 26, 0, 16),
     "pairs_u32_2p20": ("uniform u32 key-value pairs, n=2^20, bits [0,32), 4 passes",
-                       1 << 20, True, False, 0, 32),
+                       "pairs_u32", 1 << 20, 0, 32),
+    "compact_f32_2p28": ("compaction of 2^28 f32 (45% positive, 45% negative, 10% +0.0), "
+                         "keep x > 0, zero tail, count", "compact", 1 << 28, 0, 0),
+    "tile_bitonic_1024": ("1024 uniform u32 keys, one LDS bitonic tile", "bitonic", 1024, 0, 32),
+    "tile_radix_1024": ("1024 uniform u32 keys, keys-only radix sort (4 passes)",
+                        "keys_u32", 1024, 0, 32),
 }
+DEFAULT = "pairs_u32_2p28"
 
 
-def kernel_source_hash():
+def source_hash():
     h = hashlib.sha256()
-    with open(KERNEL_SOURCE, "rb") as f:
-        h.update(f.read())
+    for f in sorted(os.listdir(CSRC)):
+        with open(os.path.join(CSRC, f), "rb") as fh:
+            h.update(f.encode())
+            h.update(fh.read())
     return h.hexdigest()[:16]
 
 
 def make_inputs(name):
     import workloads
-    desc, n, pairs, is_f32, b, e = WORKLOADS[name]
+    _, kind, n, _, _ = WORKLOADS[name]
     if name == "pairs_f32_2p28":
-        keys, vals = workloads.float_pairs(n)
-    elif name == "pairs_zipf_2p26":
-        keys, vals = workloads.pairs_zipf(n)
-    else:
-        keys, vals = workloads.headline_pairs(n)
-    return keys, (vals if pairs else None)
+        return workloads.float_pairs(n)
+    if name == "pairs_zipf_2p26":
+        return workloads.pairs_zipf(n)
+    if kind == "compact":
+        return workloads.compact_input(n), None
+    if n == 1024:
+        return workloads.tile_keys(), None
+    keys, vals = workloads.headline_pairs(n)
+    return keys, (vals if kind != "keys_u32" else None)
 
 
-def cpu_baseline(keys, vals, b, e, is_f32, budget_s=12.0, sample=1 << 24):
-    """The oracle on the first `sample` elements, repeated up to ~budget_s."""
+def cpu_baseline(name, keys, vals, budget_s=12.0, sample=1 << 24):
+    """The oracle on the first `sample` elements, repeated up to about budget_s."""
     import oracle
+    _, kind, n, b, e = WORKLOADS[name]
     k = keys[:sample].copy()
     v = vals[:sample].copy() if vals is not None else None
     runs, total = 0, 0.0
     while True:
         t0 = time.perf_counter()
-        if is_f32:
+        if kind == "compact":
+            oracle.compact_positive_f32(k)
+        elif kind == "bitonic":
+            oracle.bitonic_tile(k, 1024, b, e)
+        elif kind == "pairs_f32":
             oracle.sort_f32(k, v, b, e)
         else:
             oracle.sort_u32(k, v, b, e)
         total += time.perf_counter() - t0
         runs += 1
-        if total >= budget_s or runs >= 5:
+        if total >= budget_s or runs >= (1000 if k.size <= 4096 else 5):
             break
     per_run = total / runs
-    return {"value": round(k.size / per_run / 1e9, 6), "unit": "Gkeys/s", "cores": 1,
-            "kind": "oracle",
-            "sample": "first %d elements of the same workload, %d run(s), %.2f s each; "
-                      "single-threaded C LSD counting sort (gcc -O2)" % (k.size, runs, per_run)}
+    unit = "G elements/s" if kind == "compact" else "Gkeys/s"
+    return {"value": round(k.size / per_run / 1e9, 6), "unit": unit, "cores": 1, "kind": "oracle",
+            "sample": "first %d elements of the same workload, %d run(s), %.4f s each; "
+                      "single-threaded C oracle (gcc -O2)" % (k.size, runs, per_run)}
+
+
+def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
+    import numpy as np
+    import torch
+
+    import sorting_lsd_radix_amd as rs
+
+    desc, kind, n, b, e = WORKLOADS[name]
+    print("bench: generating %s" % name, file=sys.stderr, flush=True)
+    keys, vals = make_inputs(name)
+    dev = torch.device("cuda:0")
+    stream = torch.cuda.current_stream()
+    is_f32 = kind in ("pairs_f32", "compact")
+    kin = torch.from_numpy(keys.view(np.float32) if is_f32 else keys).to(dev)
+    vin = torch.from_numpy(vals).to(dev) if vals is not None else None
+    kout = torch.empty_like(kin)
+    vout = torch.empty_like(vin) if vin is not None else None
+    count = torch.empty(1, dtype=torch.uint32, device=dev)
+    if kind == "pairs_u32":
+        need = rs.rs_sort_pairs_u32(None, None, None, None, n, b, e, None, 0)
+    elif kind == "pairs_f32":
+        need = rs.rs_sort_pairs_f32(None, None, None, None, n, b, e, None, 0)
+    elif kind == "keys_u32":
+        need = rs.rs_sort_keys_u32(None, None, n, b, e, None, 0)
+    elif kind == "compact":
+        need = rs.rs_compact_positive_f32(None, None, None, n, None, 0)
+    else:
+        need = 0
+    temp = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
+
+    def step():
+        if kind == "pairs_u32":
+            rs.rs_sort_pairs_u32(kin, kout, vin, vout, n, b, e, temp, need, stream)
+        elif kind == "pairs_f32":
+            rs.rs_sort_pairs_f32(kin, kout, vin, vout, n, b, e, temp, need, stream)
+        elif kind == "keys_u32":
+            rs.rs_sort_keys_u32(kin, kout, n, b, e, temp, need, stream)
+        elif kind == "compact":
+            rs.rs_compact_positive_f32(kin, kout, count, n, temp, need, stream)
+        else:
+            rs.rs_bitonic_tile(kin, kout, n, 1024, b, e, stream)
+
+    if copy_calibration:
+        a = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
+        c = torch.empty_like(a)
+        for _ in range(3):
+            c.copy_(a)
+        torch.cuda.synchronize()
+        del a, c
+
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+
+    rs.rs_timing_enable(True)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for _ in range(steps):
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    records = rs.rs_timing_collect()
+    rs.rs_timing_enable(False)
+    ms_per_step = total_ms / steps
+    print("bench: %s timed %d steps, %.4f ms/step" % (name, steps, ms_per_step), file=sys.stderr,
+          flush=True)
+
+    per_kernel = {}
+    for kname, ms in records:
+        per_kernel.setdefault(kname, []).append(ms)
+
+    if check:
+        ok = True
+        k_h = kout.cpu().numpy()
+        if kind == "compact":
+            import oracle
+            ref, ref_count = oracle.compact_positive_f32(keys)
+            ok = (int(count.cpu().numpy()[0]) == ref_count and
+                  bool(np.array_equal(k_h.view(np.uint32), ref.view(np.uint32))))
+        elif kind == "bitonic":
+            import oracle
+            ok = bool(np.array_equal(k_h, oracle.bitonic_tile(keys, 1024, b, e)))
+        else:
+            if kind == "pairs_f32":
+                import oracle
+                order = oracle.f32_to_order(k_h.view(np.uint32))
+            elif e - b < 32:
+                order = k_h & np.uint32(((1 << (e - b)) - 1) << b)
+            else:
+                order = k_h
+            ok = bool(np.all(order[1:] >= order[:-1]))
+            if vout is not None:
+                v_h = vout.cpu().numpy()
+                kb = keys.view(np.uint32)
+                ok = ok and bool(np.array_equal(k_h.view(np.uint32), kb[v_h]))
+                eq = order[1:] == order[:-1]
+                ok = ok and bool(np.all(v_h[1:][eq] > v_h[:-1][eq]))
+        if not ok:
+            print("bench: OUTPUT CHECK FAILED for %s" % name, file=sys.stderr, flush=True)
+            sys.exit(1)
+        print("bench: output check ok", file=sys.stderr, flush=True)
+
+    passes = (e - b + 7) // 8
+    if kind == "compact":
+        dom, bytes_per = "compact", 8
+        algo_total = 8 * n
+    elif kind == "bitonic":
+        dom, bytes_per = "bitonic", 8
+        algo_total = 8 * n
+    else:
+        dom = "onesweep"
+        bytes_per = 8 if kind == "keys_u32" else 16
+        algo_total = bytes_per * n * passes
+    dom_ms = per_kernel.get(dom, [float("nan")])
+    dom_ms = sum(dom_ms) / len(dom_ms)
+    algo_bytes = bytes_per * n
+    achieved = algo_bytes / (dom_ms * 1e-3) / 1e9
+    traffic = None
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            t = json.load(f)
+        entry = t.get(name)
+        if entry and entry.get("source_sha") == source_hash():
+            traffic = entry.get("traffic_bytes_per_launch")
+
+    if kind == "compact":
+        metric, unit, value = ("G elements/s compacted (f32, n=2^28) and % of HBM roofline",
+                               "G elements/s", n / (ms_per_step * 1e-3) / 1e9)
+    elif kind == "bitonic" or n <= 4096:
+        metric, unit, value = ("microseconds per call (1024-key tile)", "us", ms_per_step * 1e3)
+    else:
+        metric, unit, value = ("Gkeys/s sorted (u32 keys and u32 key-value, n=2^28) and % of HBM "
+                               "roofline", "Gkeys/s", n / (ms_per_step * 1e-3) / 1e9)
+    result = {
+        "metric": metric,
+        "value": round(value, 4),
+        "unit": unit,
+        "n_gpus": 1,
+        "steps": steps,
+        "warmup": warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": unit != "us",
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": {"pairs_u32": "u32", "keys_u32": "u32", "bitonic": "u32",
+                  "pairs_f32": "f32 keys (bit-pattern integer ops), u32 values",
+                  "compact": "f32 (predicate on bit patterns)"}[kind],
+        "data": "synthetic",
+        "config": {"workload": desc, "n": n, "begin_bit": b, "end_bit": e,
+                   "passes": passes if kind not in ("compact", "bitonic") else None},
+        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
+                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
+                     "kernel": dom, "algorithmic_bytes_per_launch": algo_bytes,
+                     "mean_launch_ms": round(dom_ms, 5)},
+        "whole_step_roofline_frac": round(algo_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+        "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()},
+    }
+    result["cpu_baseline"] = cpu_baseline(name, keys, vals) if with_cpu else None
+    return result
 
 
 def main():
@@ -91,7 +274,8 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=3)
-    ap.add_argument("--workload", default="pairs_u32_2p28", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default=DEFAULT, choices=sorted(WORKLOADS))
+    ap.add_argument("--all", action="store_true", help="one line per workload")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
@@ -103,126 +287,15 @@ def main():
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)
         sys.exit(2)
 
-    import numpy as np
-    import torch
-
-    import sorting_lsd_radix_amd as rs
-
-    desc, n, pairs, is_f32, b, e = WORKLOADS[args.workload]
-    print("bench: generating %s" % args.workload, file=sys.stderr, flush=True)
-    keys, vals = make_inputs(args.workload)
-    dev = torch.device("cuda:0")
-    kin = torch.from_numpy(keys.view(np.float32) if is_f32 else keys).to(dev)
-    vin = torch.from_numpy(vals).to(dev) if pairs else None
-    kout = torch.empty_like(kin)
-    vout = torch.empty_like(vin) if pairs else None
-    if is_f32:
-        need = rs.rs_sort_pairs_f32(None, None, None, None, n, b, e, None, 0)
-    elif pairs:
-        need = rs.rs_sort_pairs_u32(None, None, None, None, n, b, e, None, 0)
-    else:
-        need = rs.rs_sort_keys_u32(None, None, n, b, e, None, 0)
-    temp = torch.empty(need, dtype=torch.uint8, device=dev)
-    stream = torch.cuda.current_stream()
-
-    def step():
-        if is_f32:
-            rs.rs_sort_pairs_f32(kin, kout, vin, vout, n, b, e, temp, need, stream)
-        elif pairs:
-            rs.rs_sort_pairs_u32(kin, kout, vin, vout, n, b, e, temp, need, stream)
-        else:
-            rs.rs_sort_keys_u32(kin, kout, n, b, e, temp, need, stream)
-
-    if args.copy_calibration:
-        a = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
-        c = torch.empty_like(a)
-        for _ in range(3):
-            c.copy_(a)
-        torch.cuda.synchronize()
-        del a, c
-
-    print("bench: warmup %d" % args.warmup, file=sys.stderr, flush=True)
-    for _ in range(args.warmup):
-        step()
-    torch.cuda.synchronize()
-
-    rs.rs_timing_enable(True)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for _ in range(args.steps):
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    records = rs.rs_timing_collect()
-    rs.rs_timing_enable(False)
-    ms_per_step = total_ms / args.steps
-    print("bench: timed %d steps, %.3f ms/step" % (args.steps, ms_per_step), file=sys.stderr,
-          flush=True)
-
-    per_kernel = {}
-    for name, ms in records:
-        per_kernel.setdefault(name, []).append(ms)
-    sweep = per_kernel.get("onesweep", [])
-    sweep_ms = sum(sweep) / len(sweep) if sweep else float("nan")
-    bytes_per_key = 16 if pairs else 8
-    algo_bytes = bytes_per_key * n
-    achieved = algo_bytes / (sweep_ms * 1e-3) / 1e9
-    traffic = None
-    if os.path.exists(TRAFFIC_FILE):
-        with open(TRAFFIC_FILE) as f:
-            t = json.load(f)
-        if t.get("kernel_source_sha") == kernel_source_hash() and t.get("workload") == args.workload:
-            traffic = t.get("traffic_bytes_per_launch")
-
-    if not args.no_check:
-        k_h = kout.cpu().numpy()
-        if is_f32:
-            import oracle
-            order = oracle.f32_to_order(k_h.view(np.uint32))
-        else:
-            order = k_h & np.uint32(((1 << (e - b)) - 1) << b) if e - b < 32 else k_h
-        ok = bool(np.all(order[1:] >= order[:-1]))
-        if pairs:
-            v_h = vout.cpu().numpy()
-            ok = ok and bool(np.array_equal(k_h.view(np.uint32), keys.view(np.uint32)[v_h]))
-        if not ok:
-            print("bench: OUTPUT CHECK FAILED", file=sys.stderr, flush=True)
-            sys.exit(1)
-        print("bench: output check ok", file=sys.stderr, flush=True)
-
-    result = {
-        "metric": "Gkeys/s sorted (u32 key-value, n=2^28) and % of HBM roofline",
-        "value": round(n / (ms_per_step * 1e-3) / 1e9, 4),
-        "unit": "Gkeys/s",
-        "n_gpus": 1,
-        "steps": args.steps,
-        "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
-        "higher_is_better": True,
-        "scaling": "weak",
-        "vs_baseline": None,
-        "dtype": "u32" if not is_f32 else "f32 keys (bit-pattern integer ops), u32 values",
-        "data": "synthetic",
-        "config": {"workload": desc, "n": n, "begin_bit": b, "end_bit": e,
-                   "passes": (e - b + 7) // 8, "pairs": pairs},
-        "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
-                     "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4),
-                     "traffic": traffic,
-                     "kernel": "onesweep pass", "algorithmic_bytes_per_launch": algo_bytes,
-                     "mean_launch_ms": round(sweep_ms, 5)},
-        "whole_sort_roofline_frac": round(algo_bytes * ((e - b + 7) // 8) /
-                                          (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-        "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()},
-    }
-    if not args.no_cpu_baseline:
-        print("bench: cpu baseline", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(keys, vals, b, e, is_f32)
-    else:
-        result["cpu_baseline"] = None
-    print(json.dumps(result), flush=True)
+    names = [args.workload]
+    if args.all:
+        names = [DEFAULT] + [w for w in WORKLOADS if w != DEFAULT]
+    for name in names:
+        small = WORKLOADS[name][2] <= (1 << 20)
+        steps = max(args.steps, 100) if small else args.steps
+        res = run_workload(name, steps, args.warmup, not args.no_check, not args.no_cpu_baseline,
+                           args.copy_calibration and name == names[0])
+        print(json.dumps(res), flush=True)
 
 
 if __name__ == "__main__":

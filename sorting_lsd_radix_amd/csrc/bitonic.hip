@@ -40,6 +40,11 @@ __global__ __launch_bounds__(kBitonicBlock) void bitonic_tile_kernel(
     }
     __syncthreads();
 
+    // Step (k, j) pairs element a = 2*tid - (tid mod j) with a + j.  For
+    // j <= 64 the 64 lanes of a wave touch only their own 128 elements, so
+    // between two such steps the wave needs no block barrier: the LDS executes
+    // one wave's instructions in order, and a wave-scope fence keeps the
+    // compiler from moving the next step's reads above this step's writes.
     const uint32_t pairs = span / 2;
     for (uint32_t k = 2; k <= span; k <<= 1) {
         for (uint32_t j = k >> 1; j > 0; j >>= 1) {
@@ -54,9 +59,17 @@ __global__ __launch_bounds__(kBitonicBlock) void bitonic_tile_kernel(
                     s_item[b] = xa;
                 }
             }
-            __syncthreads();
+            const uint32_t next_j = (j > 1) ? (j >> 1) : k;   // k == span ends the network
+            if (j <= kWave && next_j <= kWave) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "wavefront");
+                __builtin_amdgcn_wave_barrier();
+                __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "wavefront");
+            } else {
+                __syncthreads();
+            }
         }
     }
+    __syncthreads();
 
     for (uint32_t i = tid; i < len; i += kBitonicBlock)
         keys_out[base + i] = s_key[static_cast<uint32_t>(s_item[i])];

@@ -8,10 +8,12 @@
 // at once).
 //
 // gfx950 mapping:
-//  * tile = BLOCK threads x 16 floats, loaded as four 16-byte vectors per
-//    lane; within a wave, row j covers 256 consecutive floats (lane l holds
-//    4 of them), so the in-tile exclusive count is: rows before + lanes before
-//    (four ballots and mbcnt) + elements before in the lane;
+//  * tile = 1024 threads x 32 floats (32768), loaded as eight 16-byte vectors
+//    per lane; within a wave, row j covers 256 consecutive floats (lane l
+//    holds 4 of them), so the in-tile exclusive count is: rows before + lanes
+//    before (four ballots and mbcnt) + elements before in the lane.  Large
+//    tiles keep the number of tiles in flight, and so the look-back walk,
+//    short;
 //  * the predicate is taken on bits: (u - 1) < 0x7F800000 is exactly
 //    x > 0.0f for IEEE binary32 including subnormals, so no flush-to-zero
 //    mode can change it;
@@ -26,9 +28,9 @@ namespace rs {
 
 namespace {
 
-constexpr int kCompBlock = 512;
-constexpr int kCompRows = 4;                               // 16-byte vectors per lane
-constexpr int kCompWaveElems = kWave * kCompRows * 4;      // 1024 floats per wave
+constexpr int kCompBlock = 1024;
+constexpr int kCompRows = 8;                               // 16-byte vectors per lane
+constexpr int kCompWaveElems = kWave * kCompRows * 4;      // 2048 floats per wave
 constexpr int kCompTile = (kCompBlock / kWave) * kCompWaveElems;
 
 __device__ __forceinline__ uint32_t keep_positive(uint32_t u) {

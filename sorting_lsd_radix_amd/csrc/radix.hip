@@ -164,6 +164,7 @@ struct PassArgs {
     uint32_t* next_states;     // look-back words of the next pass, cleared here (or null)
     uint32_t* sched;           // tile scheduler of this pass, zeroed
     uint32_t max_chunks;       // chunk-map entries per XCD group
+    uint32_t chunk_log2;       // tiles per chunk = 2^chunk_log2 (at most the blocks per group)
 };
 
 // Index of the XCD (accelerator complex die) this wave runs on.
@@ -171,19 +172,22 @@ __device__ __forceinline__ uint32_t xcd_id() {
     return static_cast<uint32_t>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20)) & 0xFu;
 }
 
-// Tile scheduler.  Tiles are handed out in chunks of kChunk consecutive tiles;
-// each XCD group works through one chunk at a time, so neighbouring tiles run
-// on the same XCD and the cache lines their digit runs share are merged in
-// that XCD's L2 before they reach memory.  Chunks are taken from one global
-// counter in order, and a group takes the tiles of its chunk in order.  The
-// tile with the smallest index among the running ones therefore has every
-// earlier tile either finished or running, so look-back always makes progress.
+// Tile scheduler.  Tiles are handed out in chunks of 2^chunk_log2 consecutive
+// tiles; each XCD group works through one chunk at a time, so neighbouring
+// tiles run on the same XCD and the cache lines their digit runs share are
+// merged in that XCD's L2 before they reach memory.  A chunk is no larger
+// than the blocks of a group, so a group runs all tiles of its chunk at once.
+// Chunks are taken from one global counter in order, and a group takes the
+// tiles of its chunk in order.  The tile with the smallest index among the
+// running ones therefore has every earlier tile either finished or running,
+// so look-back always makes progress.
 // Layout: sched[0] global chunk counter, sched[1 + g] tiles taken by group g,
 // sched[16 + g * max_chunks + j] = 1 + global index of group g's j-th chunk.
-__device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t max_chunks, uint32_t group,
+__device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t max_chunks,
+                                              uint32_t chunk_log2, uint32_t group,
                                               uint32_t tiles) {
     const uint32_t k = fetch_add_agent(&sched[1 + group], 1u);
-    const uint32_t j = k / kChunk, off = k % kChunk;
+    const uint32_t j = k >> chunk_log2, off = k & ((1u << chunk_log2) - 1u);
     if (j >= max_chunks) return tiles;   // never reached: max_chunks covers every taker
     uint32_t* slot = &sched[16 + group * max_chunks + j];
     uint32_t c;
@@ -195,7 +199,7 @@ __device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t max_chun
         while ((v = load_state(slot)) == 0u) __builtin_amdgcn_s_sleep(1);
         c = v - 1u;
     }
-    const uint64_t t = static_cast<uint64_t>(c) * kChunk + off;
+    const uint64_t t = (static_cast<uint64_t>(c) << chunk_log2) + off;
     return t < tiles ? static_cast<uint32_t>(t) : tiles;
 }
 
@@ -255,7 +259,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     for (;;) {
         // The tile is taken only when the block can start on it at once, so
         // its count is published as early as possible.
-        if (tid == 0) s_tile = next_tile(a.sched, a.max_chunks, group, tiles);
+        if (tid == 0) s_tile = next_tile(a.sched, a.max_chunks, a.chunk_log2, group, tiles);
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
         __syncthreads();
         const uint32_t tile = s_tile;
@@ -467,8 +471,8 @@ constexpr uint32_t kMaxResidentBlocks = 4096;
 SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
     SortLayout L{};
     L.tiles = static_cast<uint32_t>((n + kSortTile - 1) / kSortTile);
-    // a group's j-th chunk exists for j <= chunks + (its blocks) / kChunk
-    L.max_chunks = (L.tiles + kChunk - 1) / kChunk + kMaxResidentBlocks / kChunk + 2;
+    // a group takes at most tiles + (its blocks) chunk slots, whatever the chunk size
+    L.max_chunks = L.tiles + kMaxResidentBlocks + 2;
     L.sched_words = static_cast<uint32_t>(align_up((16 + kGroups * L.max_chunks) * 4) / 4);
     const size_t states_bytes = align_up(static_cast<size_t>(L.tiles) * kRadix * 4);
     size_t off = 0;
@@ -518,7 +522,11 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     auto kern = onesweep_kernel<BLOCK, ITEMS, kSortLookback, PAIRS, FI, FO>;
     if (resident == 0) resident = resident_blocks(kern, BLOCK);
     const uint32_t grid = a.tiles < resident ? a.tiles : resident;
-    kern<<<dim3(grid), BLOCK, 0, s>>>(a);
+    // chunk: the largest power of two not above the blocks per group, capped
+    PassArgs b = a;
+    b.chunk_log2 = 0;
+    while ((2u << b.chunk_log2) <= grid / kGroups && (2u << b.chunk_log2) <= kChunk) ++b.chunk_log2;
+    kern<<<dim3(grid), BLOCK, 0, s>>>(b);
     return hipGetLastError();
 }
 

@@ -18,7 +18,8 @@ from gpu_helpers import (gpu_bitonic, gpu_compact, gpu_sort_keys_u32, gpu_sort_p
 
 pytestmark = pytest.mark.gpu
 
-TILE = 8192  # keys per tile of the one-sweep pass
+TILE = 16384  # keys per tile of the one-sweep pass
+CTILE = 32768  # floats per tile of the compaction
 SIZES = [1, 2, 63, 64, 65, 1000, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17]
 RANGES = [(0, 32), (0, 16), (8, 24), (4, 13), (0, 1), (31, 32), (7, 7), (0, 8), (24, 32)]
 
@@ -107,8 +108,8 @@ def test_pairs_f32_specials_ladder():
     assert np.array_equal(v, rv) and np.array_equal(k.view(np.uint32), rk.view(np.uint32))
 
 
-@pytest.mark.parametrize("n", [1, 3, 4, 5, 63, 64, 65, 1000, 8191, 8192, 8193, 3 * 8192 + 5,
-                               (1 << 20) + 3])
+@pytest.mark.parametrize("n", [1, 3, 4, 5, 63, 64, 65, 1000, CTILE - 1, CTILE, CTILE + 1,
+                               3 * CTILE + 5, (1 << 20) + 3])
 def test_compaction_sizes(n):
     print("compact n=%d" % n, flush=True)
     x = workloads.signed_mix_f32(n, seed=n)
@@ -120,7 +121,7 @@ def test_compaction_sizes(n):
 
 @pytest.mark.parametrize("kind", ["all_positive", "none_positive", "specials", "zeros"])
 def test_compaction_cases(kind):
-    n = 2 * 8192 + 77
+    n = 2 * CTILE + 77
     r = rng(21)
     if kind == "all_positive":
         x = np.abs(r.standard_normal(n).astype(np.float32)) + np.float32(0.5)
