@@ -8,6 +8,9 @@
 namespace rs {
 
 constexpr int kWave = 64;          // CDNA wavefront width
+
+// 16-byte vector of u32 (a clang vector type, usable with the nontemporal builtins)
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRadixBits = 8;      // digit width of every sort pass
 constexpr int kRadix = 1 << kRadixBits;
 

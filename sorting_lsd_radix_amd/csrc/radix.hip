@@ -34,6 +34,8 @@ constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
 constexpr int kSortLookback = 8;       // earlier tiles read per look-back batch
 constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
+constexpr bool kRankByMask = false;    // in-wave rank by LDS lane masks (else by ballots); the
+                                       // masks serialise on skewed digits, the ballots do not
 constexpr int kGroups = 8;             // XCDs
 
 constexpr int kUpBlock = 256;
@@ -91,16 +93,20 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
     for (int i = threadIdx.x; i < kMaxPasses * kRadix * kUpSub; i += kUpBlock) s_hist[i] = 0u;
     __syncthreads();
 
+    // Each block reads one contiguous chunk of whole 16-byte vectors, four
+    // rows of kUpBlock vectors at a time, with non-temporal loads (the keys
+    // are not read again before the first pass evicts them anyway).
     const uint32_t sub = threadIdx.x % kUpSub;
     const uint32_t nvec = n / 4;
-    const uint4* k4 = reinterpret_cast<const uint4*>(keys);
-    const uint32_t stride = gridDim.x * kUpBlock;
-    uint32_t i = blockIdx.x * kUpBlock + threadIdx.x;
-    // four 16-byte loads in flight per thread before the LDS counting
-    for (; i + 3 * stride < nvec; i += 4 * stride) {
-        uint4 q[4];
+    const uint32_t per_block = (nvec + gridDim.x - 1) / gridDim.x;
+    const uint32_t begin = blockIdx.x * per_block;
+    const uint32_t end = (begin + per_block < nvec) ? begin + per_block : nvec;
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
+    uint32_t i = begin + threadIdx.x;
+    for (; i + 3 * kUpBlock < end; i += 4 * kUpBlock) {
+        u32x4 q[4];
 #pragma unroll
-        for (int u = 0; u < 4; ++u) q[u] = k4[i + u * stride];
+        for (int u = 0; u < 4; ++u) q[u] = __builtin_nontemporal_load(&k4[i + u * kUpBlock]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
             count_key<FLIP>(s_hist, q[u].x, pd, sub);
@@ -109,8 +115,8 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
             count_key<FLIP>(s_hist, q[u].w, pd, sub);
         }
     }
-    for (; i < nvec; i += stride) {
-        const uint4 q = k4[i];
+    for (; i < end; i += kUpBlock) {
+        const u32x4 q = __builtin_nontemporal_load(&k4[i]);
         count_key<FLIP>(s_hist, q.x, pd, sub);
         count_key<FLIP>(s_hist, q.y, pd, sub);
         count_key<FLIP>(s_hist, q.z, pd, sub);
@@ -212,9 +218,10 @@ __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint
                                           uint32_t (&x)[ITEMS]) {
     const uint32_t first = tile * TILE + wave * (kWave * ITEMS) + lane;
     if (tile * TILE + TILE <= n) {
-        const uint32_t* p = src + first;   // row offsets fold into the load instruction
+        // row offsets fold into the load; non-temporal: each key is read once per pass
+        const uint32_t* p = src + first;
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) x[j] = p[j * kWave];
+        for (int j = 0; j < ITEMS; ++j) x[j] = __builtin_nontemporal_load(&p[j * kWave]);
     } else {
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
@@ -231,12 +238,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
-    static_assert((TILE & (TILE - 1)) == 0, "tile must be a power of two");
+    static_assert((TILE & (TILE - 1)) == 0 && TILE <= 32768, "tile: a power of two, 16-bit positions");
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
 
     // One staging buffer: the keys in digit order, then the values in digit order.
     __shared__ uint32_t s_buf[TILE];
     __shared__ uint32_t s_off[WAVES * kRadix];   // per-wave digit counters, then offsets
+    // per-wave lane masks of each digit (rank by mask); all zero between slots
+    __shared__ uint64_t s_mask[kRankByMask ? WAVES * kRadix : 1];
     __shared__ uint32_t s_adjust[kRadix];
     __shared__ uint32_t s_wsum[2][kRadix / kWave];
     __shared__ uint32_t s_tile;
@@ -255,10 +264,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
+    if constexpr (kRankByMask)
+        for (uint32_t i = lane; i < kRadix; i += kWave) s_mask[wave * kRadix + i] = 0ull;
 
     for (;;) {
-        // The tile is taken only when the block can start on it at once, so
-        // its count is published as early as possible.
+        // A tile is taken only when the block can start on it at once: the
+        // time from taking a tile to publishing its count delays every later
+        // tile's look-back (taking it earlier, or prefetching the next tile
+        // during the scatter, measured slower).
         if (tid == 0) s_tile = next_tile(a.sched, a.max_chunks, a.chunk_log2, group, tiles);
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
         __syncthreads();
@@ -281,17 +294,43 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
         }
 
         // ---- stable rank inside the wave --------------------------------------
-        uint32_t pos[ITEMS];   // rank in the wave, later the position in the tile
+        // rank in the wave, later the position in the tile: 16 bits, two per register
+        uint32_t pos[ITEMS / 2];
         uint32_t* my_count = s_off + wave * kRadix;
+        uint64_t* my_mask = s_mask + (kRankByMask ? wave * kRadix : 0);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
-            const uint64_t others = lanes_with_other_digit(d);
-            const uint32_t below = lane - count_below(others);      // same digit, lower lane
-            const uint32_t before = my_count[d];
-            if (below == 0)
-                my_count[d] = before + kWave - static_cast<uint32_t>(__popcll(others));
-            pos[j] = before + below;
+            uint32_t below, group;
+            uint32_t before;
+            if constexpr (kRankByMask) {
+                // Each lane ORs its bit into this wave's mask of digit d; once
+                // the OR instruction has run for every lane (one wave's LDS
+                // instructions execute in order) the mask is exactly the set
+                // of lanes holding d, whatever order the lanes were served in.
+                // The mask and the digit's counter are read together, so a
+                // slot costs one LDS round trip.
+                uint64_t* m = &my_mask[d];
+                __hip_atomic_fetch_or(m, 1ull << lane, __ATOMIC_RELAXED,
+                                      __HIP_MEMORY_SCOPE_WORKGROUP);
+                const uint64_t peers = __hip_atomic_load(m, __ATOMIC_RELAXED,
+                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
+                before = my_count[d];
+                below = count_below(peers);
+                group = static_cast<uint32_t>(__popcll(peers));
+                if (below == 0) {   // the lowest lane of the group clears the mask
+                    __hip_atomic_store(m, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                    my_count[d] = before + group;
+                }
+            } else {
+                before = my_count[d];
+                const uint64_t others = lanes_with_other_digit(d);
+                below = lane - count_below(others);      // same digit, lower lane
+                group = kWave - static_cast<uint32_t>(__popcll(others));
+                if (below == 0) my_count[d] = before + group;
+            }
+            if (j % 2 == 0) pos[j / 2] = before + below;
+            else pos[j / 2] |= (before + below) << 16;
             // the slots are chained through the LDS counters anyway; keeping the
             // scheduler from interleaving them keeps register pressure low
             __builtin_amdgcn_sched_barrier(0);
@@ -369,8 +408,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
             asm volatile("" : "+v"(key));
             const uint32_t d = __builtin_amdgcn_ubfe(key, shift, width);
             // (the mask never changes a consistent position; it keeps the store in the tile)
-            pos[j] = (s_off[wave * kRadix + d] + pos[j]) & (TILE - 1);
-            s_buf[pos[j]] = key;
+            const uint32_t sh = 16 * (j % 2);
+            const uint32_t p = (s_off[wave * kRadix + d] + ((pos[j / 2] >> sh) & 0xFFFFu)) & (TILE - 1);
+            pos[j / 2] = (pos[j / 2] & ~(0xFFFFu << sh)) | (p << sh);
+            s_buf[p] = key;
         }
 
         // ---- decoupled look-back: same-digit keys in all earlier tiles --------
@@ -436,7 +477,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
         if (PAIRS) {
             __syncthreads();   // every key has been read from the staging buffer
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) s_buf[pos[j]] = v[j];
+            for (int j = 0; j < ITEMS; ++j) s_buf[(pos[j / 2] >> (16 * (j % 2))) & 0xFFFFu] = v[j];
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < ITEMS; ++r) {
