@@ -34,9 +34,9 @@ constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
 constexpr int kSortLookback = 8;       // earlier tiles read per look-back batch
 constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
-constexpr bool kRankByMask = false;    // in-wave rank by LDS lane masks (else by ballots); the
-                                       // masks serialise on skewed digits, the ballots do not
 constexpr int kGroups = 8;             // XCDs
+// Word 3 of a raw buffer descriptor on gfx9-family chips (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
 
 constexpr int kUpBlock = 256;
 constexpr int kUpSub = 8;          // sub-histograms per digit (spreads LDS atomics)
@@ -181,12 +181,14 @@ __device__ __forceinline__ uint32_t xcd_id() {
 // Tile scheduler.  Tiles are handed out in chunks of 2^chunk_log2 consecutive
 // tiles; each XCD group works through one chunk at a time, so neighbouring
 // tiles run on the same XCD and the cache lines their digit runs share are
-// merged in that XCD's L2 before they reach memory.  A chunk is no larger
-// than the blocks of a group, so a group runs all tiles of its chunk at once.
-// Chunks are taken from one global counter in order, and a group takes the
-// tiles of its chunk in order.  The tile with the smallest index among the
-// running ones therefore has every earlier tile either finished or running,
-// so look-back always makes progress.
+// merged in that XCD's L2 before they reach memory.  Chunks go to whichever
+// group needs one next, from one global counter, which keeps the tiles in
+// flight close together in index order (short look-backs) and lets a faster
+// XCD take more chunks.  A chunk is no larger than the blocks of a group, so
+// a group runs all tiles of its chunk at once, and a block starts every tile
+// it takes at once.  The smallest unfinished tile is therefore either running
+// (every earlier tile is done, so its look-back ends) or not yet handed out,
+// and then a block is free to take it, so look-back always makes progress.
 // Layout: sched[0] global chunk counter, sched[1 + g] tiles taken by group g,
 // sched[16 + g * max_chunks + j] = 1 + global index of group g's j-th chunk.
 __device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t max_chunks,
@@ -237,6 +239,7 @@ template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLI
 __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
+    constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
     static_assert((TILE & (TILE - 1)) == 0 && TILE <= 32768, "tile: a power of two, 16-bit positions");
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
@@ -244,11 +247,9 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     // One staging buffer: the keys in digit order, then the values in digit order.
     __shared__ uint32_t s_buf[TILE];
     __shared__ uint32_t s_off[WAVES * kRadix];   // per-wave digit counters, then offsets
-    // per-wave lane masks of each digit (rank by mask); all zero between slots
-    __shared__ uint64_t s_mask[kRankByMask ? WAVES * kRadix : 1];
     __shared__ uint32_t s_adjust[kRadix];
     __shared__ uint32_t s_wsum[2][kRadix / kWave];
-    __shared__ uint32_t s_tile;
+    __shared__ uint32_t s_next;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
@@ -264,25 +265,24 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
-    if constexpr (kRankByMask)
-        for (uint32_t i = lane; i < kRadix; i += kWave) s_mask[wave * kRadix + i] = 0ull;
 
     for (;;) {
         // A tile is taken only when the block can start on it at once: the
         // time from taking a tile to publishing its count delays every later
-        // tile's look-back (taking it earlier, or prefetching the next tile
-        // during the scatter, measured slower).
-        if (tid == 0) s_tile = next_tile(a.sched, a.max_chunks, a.chunk_log2, group, tiles);
+        // tile's look-back.
+        if (tid == 0) s_next = next_tile(a.sched, a.max_chunks, a.chunk_log2, group, tiles);
+        // Only this wave reads and writes its counters during the rank, and the
+        // previous tile's readers of s_off all passed a barrier since.
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
         __syncthreads();
-        const uint32_t tile = s_tile;
+        const uint32_t tile = s_next;
         if (tile >= tiles) break;   // uniform: no tiles left
         uint32_t k[ITEMS];
         load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
         const uint32_t tile_base = tile * TILE;
         const uint32_t valid = (n - tile_base < static_cast<uint32_t>(TILE)) ? n - tile_base : TILE;
         const bool full = (valid == static_cast<uint32_t>(TILE));
-        const uint32_t first = tile_base + wave * (kWave * ITEMS) + lane;
+        const uint32_t first = tile_base + wave * WAVE_KEYS + lane;
         if (FLIP_IN) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) k[j] = float_to_sortable(k[j]);
@@ -297,38 +297,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
         // rank in the wave, later the position in the tile: 16 bits, two per register
         uint32_t pos[ITEMS / 2];
         uint32_t* my_count = s_off + wave * kRadix;
-        uint64_t* my_mask = s_mask + (kRankByMask ? wave * kRadix : 0);
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
-            uint32_t below, group;
-            uint32_t before;
-            if constexpr (kRankByMask) {
-                // Each lane ORs its bit into this wave's mask of digit d; once
-                // the OR instruction has run for every lane (one wave's LDS
-                // instructions execute in order) the mask is exactly the set
-                // of lanes holding d, whatever order the lanes were served in.
-                // The mask and the digit's counter are read together, so a
-                // slot costs one LDS round trip.
-                uint64_t* m = &my_mask[d];
-                __hip_atomic_fetch_or(m, 1ull << lane, __ATOMIC_RELAXED,
-                                      __HIP_MEMORY_SCOPE_WORKGROUP);
-                const uint64_t peers = __hip_atomic_load(m, __ATOMIC_RELAXED,
-                                                         __HIP_MEMORY_SCOPE_WORKGROUP);
-                before = my_count[d];
-                below = count_below(peers);
-                group = static_cast<uint32_t>(__popcll(peers));
-                if (below == 0) {   // the lowest lane of the group clears the mask
-                    __hip_atomic_store(m, 0ull, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                    my_count[d] = before + group;
-                }
-            } else {
-                before = my_count[d];
-                const uint64_t others = lanes_with_other_digit(d);
-                below = lane - count_below(others);      // same digit, lower lane
-                group = kWave - static_cast<uint32_t>(__popcll(others));
-                if (below == 0) my_count[d] = before + group;
-            }
+            const uint32_t before = my_count[d];
+            const uint64_t others = lanes_with_other_digit(d);
+            const uint32_t below = lane - count_below(others);      // same digit, lower lane
+            const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
+            if (below == 0) my_count[d] = before + group_size;
             if (j % 2 == 0) pos[j / 2] = before + below;
             else pos[j / 2] |= (before + below) << 16;
             // the slots are chained through the LDS counters anyway; keeping the
@@ -348,7 +324,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
             }
         }
         // the padding of a partial tile sits in the last digit; it is not published
-        const uint32_t pads = full ? 0u : static_cast<uint32_t>(TILE) - valid;
+        const uint32_t pads = static_cast<uint32_t>(TILE) - valid;
         const uint32_t real = (tid == last_digit) ? count - pads : count;
         if (tid < kRadix)
             store_state(&states[tile * kRadix + tid],
@@ -456,7 +432,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
 
         // ---- scatter each digit run to consecutive addresses ----------------------
         // Slot r of this thread is tile position r * BLOCK + tid; its digit is
-        // kept (four per register) for the value scatter.
+        // kept (four per register) for the value scatter.  Stores go through
+        // buffer descriptors whose size is n elements: the hardware drops a
+        // store past the end, which is where every pad of a partial tile
+        // lands (pads rank after the last real key of the last digit, whose
+        // run ends at n), so no slot needs a branch and the LDS reads of all
+        // slots can be in flight together.
+        const __amdgpu_buffer_rsrc_t out_keys =
+            __builtin_amdgcn_make_buffer_rsrc(dst_keys, 0, static_cast<int>(n * 4u), kBufferWord3);
         uint32_t digits[PAIRS ? ITEMS / 4 : 1];
 #pragma unroll
         for (int r = 0; r < ITEMS; ++r) {
@@ -467,14 +450,14 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
                 if (r % 4 == 0) digits[r / 4] = d;
                 else digits[r / 4] |= d << (8 * (r % 4));
             }
-            if (full || i < valid) {
-                const uint32_t dst = i + s_adjust[d];
-                if (dst < n)   // always true for consistent counts; guards the store
-                    dst_keys[dst] = FLIP_OUT ? sortable_to_float(key) : key;
-            }
+            const uint32_t dst = i + s_adjust[d];
+            __builtin_amdgcn_raw_buffer_store_b32(FLIP_OUT ? sortable_to_float(key) : key, out_keys,
+                                                  static_cast<int>(dst * 4u), 0, 0);
             if (PAIRS && r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounds live registers
         }
         if (PAIRS) {
+            const __amdgpu_buffer_rsrc_t out_vals =
+                __builtin_amdgcn_make_buffer_rsrc(dst_vals, 0, static_cast<int>(n * 4u), kBufferWord3);
             __syncthreads();   // every key has been read from the staging buffer
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) s_buf[(pos[j / 2] >> (16 * (j % 2))) & 0xFFFFu] = v[j];
@@ -482,14 +465,12 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
 #pragma unroll
             for (int r = 0; r < ITEMS; ++r) {
                 const uint32_t i = r * BLOCK + tid;
-                if (full || i < valid) {
-                    const uint32_t d = (digits[r / 4] >> (8 * (r % 4))) & 0xFFu;
-                    const uint32_t dst = i + s_adjust[d];
-                    if (dst < n) dst_vals[dst] = s_buf[i];
-                }
+                const uint32_t d = (digits[r / 4] >> (8 * (r % 4))) & 0xFFu;
+                const uint32_t dst = i + s_adjust[d];
+                __builtin_amdgcn_raw_buffer_store_b32(s_buf[i], out_vals, static_cast<int>(dst * 4u), 0, 0);
             }
         }
-        // the next iteration rewrites s_off and s_buf only after a barrier
+        // the next iteration rewrites s_buf and s_adjust only after a barrier
     }
 }
 
@@ -563,8 +544,8 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     auto kern = onesweep_kernel<BLOCK, ITEMS, kSortLookback, PAIRS, FI, FO>;
     if (resident == 0) resident = resident_blocks(kern, BLOCK);
     const uint32_t grid = a.tiles < resident ? a.tiles : resident;
-    // chunk: the largest power of two not above the blocks per group, capped
     PassArgs b = a;
+    // chunk: the largest power of two not above the blocks per group, capped
     b.chunk_log2 = 0;
     while ((2u << b.chunk_log2) <= grid / kGroups && (2u << b.chunk_log2) <= kChunk) ++b.chunk_log2;
     kern<<<dim3(grid), BLOCK, 0, s>>>(b);
