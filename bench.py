@@ -9,8 +9,9 @@ inputs, outputs and temp already resident in HBM.  Prints one JSON line.
                   [--no-cpu-baseline] [--no-check] [--copy-calibration]
 
 The roofline entry is for the dominant kernel of the workload (the one-sweep
-pass for sorts, the compaction kernel for compaction): its algorithmic bytes
-per launch over its mean duration, timed with HIP events that the library
+pass for sorts, the one-workgroup tile sort for sorts of at most 16384 keys,
+the compaction kernel for compaction): its algorithmic bytes per launch over
+its mean duration, timed with HIP events that the library
 records around each of its launches on the call's stream during the timed
 steps.  Algorithmic bytes: 16 B per key per pass for key-value sorts (read and
 write key and value), 8 B for keys-only sorts, 8 B per element for compaction
@@ -29,6 +30,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
+TILE_SORT_MAX = 16384  # sorts up to this size run in one workgroup (one launch)
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 CSRC = os.path.join(ROOT, "sorting_lsd_radix_amd", "csrc")
@@ -217,6 +219,11 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
     elif kind == "bitonic":
         dom, bytes_per = "bitonic", 8
         algo_total = 8 * n
+    elif n <= TILE_SORT_MAX:
+        # the whole sort in one workgroup: the keys (and values) cross HBM once each way
+        dom = "tile_sort"
+        bytes_per = 8 if kind == "keys_u32" else 16
+        algo_total = bytes_per * n
     else:
         dom = "onesweep"
         bytes_per = 8 if kind == "keys_u32" else 16

@@ -71,6 +71,9 @@ typedef enum rs_status {
  *          it are carried but ignored; equal fields keep input order.
  *          begin_bit == end_bit copies the input.
  * d_temp, temp_bytes: see the query idiom above.
+ * Up to 16384 keys the whole sort runs in one workgroup in LDS (one launch,
+ * the temp buffer is not touched); above, one digit-count launch and one
+ * launch per digit pass.
  */
 rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n,
                            int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
@@ -145,7 +148,8 @@ typedef enum rs_kernel_id {
     RS_KERNEL_COMPACT_INIT = 3, /* clears the compaction's counter and states */
     RS_KERNEL_COMPACT = 4,      /* single-pass compaction */
     RS_KERNEL_BITONIC = 5,      /* LDS bitonic tiles */
-    RS_KERNEL_COPY = 6          /* device copy for an empty bit range */
+    RS_KERNEL_COPY = 6,         /* device copy for an empty bit range */
+    RS_KERNEL_TILE_SORT = 7     /* whole sort of n <= 16384 keys in one block */
 } rs_kernel_id;
 
 rs_status rs_timing_enable(int enable);

@@ -41,8 +41,9 @@ RS_KERNEL_COMPACT_INIT = 3
 RS_KERNEL_COMPACT = 4
 RS_KERNEL_BITONIC = 5
 RS_KERNEL_COPY = 6
+RS_KERNEL_TILE_SORT = 7
 KERNEL_NAMES = {0: "upsweep", 1: "onesweep", 2: "sort_init", 3: "compact_init",
-                4: "compact", 5: "bitonic", 6: "copy"}
+                4: "compact", 5: "bitonic", 6: "copy", 7: "tile_sort"}
 
 EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32",
                     "rs_compact_positive_f32", "rs_bitonic_tile", "rs_status_string",

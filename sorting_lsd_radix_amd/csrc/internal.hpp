@@ -16,9 +16,6 @@ void timing_after(hipStream_t s);
 
 // ---- radix sort ---------------------------------------------------------------
 
-// Keys per tile of the one-sweep pass kernel.
-uint32_t onesweep_tile_keys();
-
 // Temp bytes for a sort of n keys with `passes` 8-bit passes.
 size_t sort_temp_bytes(uint64_t n, bool pairs, int passes);
 

@@ -32,6 +32,8 @@ namespace {
 constexpr int kSortBlock = 1024;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
+// Up to this many keys the whole sort runs in one block, in LDS.
+constexpr uint32_t kTileSortMax = kSortTile;
 constexpr int kSortLookback = 8;       // earlier tiles read per look-back batch
 constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
 constexpr int kGroups = 8;             // XCDs
@@ -474,6 +476,125 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     }
 }
 
+// ---------------------------------------------------------------------------
+// One-block sort of n <= kTileSortMax keys (and values): every pass runs in
+// LDS, with the same stable in-wave rank as the one-sweep pass and no global
+// counts, look-back or temp storage.  Pass p re-lays the tile out in the
+// order of digit p; that order is pass p + 1's input order, which is the LSD
+// recurrence of "WebGPU Unleashed", 4.1 (each pass a stable counting sort).
+// Pads (key 0xFFFFFFFF after the flip) fill the tile past n; they carry the
+// last digit of every pass and come after every real key in input order, so
+// they stay at positions n.. in every pass and are never stored.
+// ---------------------------------------------------------------------------
+template <int BLOCK, int ITEMS, bool PAIRS, bool FLIP>
+__global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __restrict__ keys_in,
+                                                          uint32_t* __restrict__ keys_out,
+                                                          const uint32_t* __restrict__ vals_in,
+                                                          uint32_t* __restrict__ vals_out,
+                                                          uint32_t n, PassDigits pd) {
+    constexpr int WAVES = BLOCK / kWave;
+    constexpr int TILE = BLOCK * ITEMS;
+    constexpr int WAVE_KEYS = kWave * ITEMS;
+    static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
+    static_assert(TILE <= 32768 && ITEMS % 2 == 0, "16-bit positions, two per register");
+
+    __shared__ uint32_t s_keys[TILE];
+    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    __shared__ uint32_t s_off[WAVES * kRadix];   // per-wave digit counters, then offsets
+    __shared__ uint32_t s_wsum[kRadix / kWave];
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t wave = tid / kWave;
+    const uint32_t first = wave * WAVE_KEYS + lane;   // row j of this lane: first + 64 j
+
+    uint32_t k[ITEMS];
+    uint32_t v[PAIRS ? ITEMS : 1];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t i = first + j * kWave;
+        if (i < n) {
+            k[j] = FLIP ? float_to_sortable(keys_in[i]) : keys_in[i];
+            if constexpr (PAIRS) v[j] = vals_in[i];
+        } else {
+            k[j] = 0xFFFFFFFFu;
+            if constexpr (PAIRS) v[j] = 0u;
+        }
+    }
+
+    for (uint32_t p = 0; p < pd.passes; ++p) {
+        const uint32_t shift = pd.shift[p], width = pd.width[p];
+        // this wave's counters; their readers in the previous pass all passed a barrier since
+        for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
+
+        uint32_t pos[ITEMS / 2];
+        uint32_t* my_count = s_off + wave * kRadix;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+            const uint32_t before = my_count[d];
+            const uint64_t others = lanes_with_other_digit(d);
+            const uint32_t below = lane - count_below(others);
+            const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
+            if (below == 0) my_count[d] = before + group_size;
+            if (j % 2 == 0) pos[j / 2] = before + below;
+            else pos[j / 2] |= (before + below) << 16;
+            __builtin_amdgcn_sched_barrier(0);
+        }
+        __syncthreads();
+
+        // per digit: offsets of each wave, then the tile-wide exclusive scan
+        uint32_t count = 0;
+        if (tid < kRadix) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const uint32_t c = s_off[w * kRadix + tid];
+                s_off[w * kRadix + tid] = count;
+                count += c;
+            }
+            const uint32_t inc = wave_inclusive_sum(count);
+            if (lane == kWave - 1) s_wsum[wave] = inc;
+            count = inc - count;   // exclusive within this wave's 64 digits
+        }
+        __syncthreads();
+        if (tid < kRadix) {
+            uint32_t start = count;
+#pragma unroll
+            for (int w = 0; w < kRadix / kWave; ++w)
+                if (w < static_cast<int>(wave)) start += s_wsum[w];
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) s_off[w * kRadix + tid] += start;
+        }
+        __syncthreads();
+
+        // re-lay the tile out in digit order; read it back as the next input order
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+            const uint32_t q = (s_off[wave * kRadix + d] + ((pos[j / 2] >> (16 * (j % 2))) & 0xFFFFu)) &
+                               (TILE - 1);
+            s_keys[q] = k[j];
+            if constexpr (PAIRS) s_vals[q] = v[j];
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            k[j] = s_keys[first + j * kWave];
+            if constexpr (PAIRS) v[j] = s_vals[first + j * kWave];
+        }
+        // the next pass writes s_keys and s_vals only after two more barriers
+    }
+
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const uint32_t i = first + j * kWave;
+        if (i < n) {
+            keys_out[i] = FLIP ? sortable_to_float(k[j]) : k[j];
+            if constexpr (PAIRS) vals_out[i] = v[j];
+        }
+    }
+}
+
 // Temp layout (every piece 256-byte aligned):
 //   bins     [kMaxPasses][256] u32   global digit counts of each pass
 //   sched    [kMaxPasses][sched_words] u32   tile schedulers (see next_tile)
@@ -560,6 +681,27 @@ hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream
     return launch_pass_t<kSortBlock, kSortItems, PAIRS, false, false>(a, s);
 }
 
+template <int BLOCK, int ITEMS, bool PAIRS>
+void launch_tile_sort_t(const uint32_t* ki, uint32_t* ko, const uint32_t* vi, uint32_t* vo,
+                        uint32_t n, const PassDigits& pd, bool flip, hipStream_t s) {
+    if (flip)
+        tile_sort_kernel<BLOCK, ITEMS, PAIRS, true><<<1, BLOCK, 0, s>>>(ki, ko, vi, vo, n, pd);
+    else
+        tile_sort_kernel<BLOCK, ITEMS, PAIRS, false><<<1, BLOCK, 0, s>>>(ki, ko, vi, vo, n, pd);
+}
+
+// One block, the smallest tile shape that holds n keys.
+template <bool PAIRS>
+void launch_tile_sort(const uint32_t* ki, uint32_t* ko, const uint32_t* vi, uint32_t* vo,
+                      uint32_t n, const PassDigits& pd, bool flip, hipStream_t s) {
+    if (n <= 256 * 4)
+        launch_tile_sort_t<256, 4, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+    else if (n <= 512 * 8)
+        launch_tile_sort_t<512, 8, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+    else
+        launch_tile_sort_t<kSortBlock, kSortItems, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+}
+
 int upsweep_grid(uint32_t n) {
     const int cus = device_cus();
     const uint64_t vec_per_block = static_cast<uint64_t>(kUpBlock) * 16;   // >= 16 uint4 per thread
@@ -571,9 +713,8 @@ int upsweep_grid(uint32_t n) {
 
 }  // namespace
 
-uint32_t onesweep_tile_keys() { return kSortTile; }
-
 size_t sort_temp_bytes(uint64_t n, bool pairs, int passes) {
+    if (n <= kTileSortMax) return kAlign;   // the one-block sort needs no temp storage
     return sort_layout(n, pairs, passes).total;
 }
 
@@ -594,6 +735,25 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
                        void* temp, hipStream_t stream) {
     const bool pairs = vals_in != nullptr;
     const int passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
+    PassDigits pd{};
+    pd.passes = static_cast<uint32_t>(passes);
+    for (int p = 0; p < passes; ++p) {
+        const int s = begin_bit + kRadixBits * p;
+        const int w = (end_bit - s < kRadixBits) ? end_bit - s : kRadixBits;
+        pd.shift[p] = static_cast<uint32_t>(s);
+        pd.mask[p] = (1u << w) - 1u;
+        pd.width[p] = static_cast<uint32_t>(w);
+    }
+    if (n <= kTileSortMax) {
+        timing_before(stream, RS_KERNEL_TILE_SORT);
+        if (pairs)
+            launch_tile_sort<true>(keys_in, keys_out, vals_in, vals_out, n, pd, is_f32, stream);
+        else
+            launch_tile_sort<false>(keys_in, keys_out, nullptr, nullptr, n, pd, is_f32, stream);
+        const hipError_t e = hipGetLastError();
+        timing_after(stream);
+        return e;
+    }
     const SortLayout L = sort_layout(n, pairs, passes);
     char* base = static_cast<char*>(temp);
     uint32_t* bins = reinterpret_cast<uint32_t*>(base + L.bins);
@@ -607,15 +767,6 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
                                     RS_KERNEL_SORT_INIT);
     if (e != hipSuccess) return e;
 
-    PassDigits pd{};
-    pd.passes = static_cast<uint32_t>(passes);
-    for (int p = 0; p < passes; ++p) {
-        const int s = begin_bit + kRadixBits * p;
-        const int w = (end_bit - s < kRadixBits) ? end_bit - s : kRadixBits;
-        pd.shift[p] = static_cast<uint32_t>(s);
-        pd.mask[p] = (1u << w) - 1u;
-        pd.width[p] = static_cast<uint32_t>(w);
-    }
     timing_before(stream, RS_KERNEL_UPSWEEP);
     if (is_f32)
         upsweep_kernel<true><<<upsweep_grid(n), kUpBlock, 0, stream>>>(keys_in, n, pd, bins);

@@ -18,9 +18,15 @@ from gpu_helpers import (gpu_bitonic, gpu_compact, gpu_sort_keys_u32, gpu_sort_p
 
 pytestmark = pytest.mark.gpu
 
-TILE = 16384  # keys per tile of the one-sweep pass
+# Sort paths: up to TILE keys one workgroup sorts in LDS (tile shapes of 1024,
+# 4096 and 16384 keys); above, the one-sweep passes use TILE-key tiles.  LARGE
+# is the first size at which every CU gets a tile.
+TILE = 16384
+STILE = 4096
+LARGE = 256 * TILE
 CTILE = 32768  # floats per tile of the compaction
-SIZES = [1, 2, 63, 64, 65, 1000, TILE - 1, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17]
+SIZES = [1, 2, 63, 64, 65, 1000, 1024, 1025, STILE, STILE + 1, TILE - 1, TILE, TILE + 1,
+         3 * TILE + 17, (1 << 20) + 17, LARGE - 1, LARGE, LARGE + 17]
 RANGES = [(0, 32), (0, 16), (8, 24), (4, 13), (0, 1), (31, 32), (7, 7), (0, 8), (24, 32)]
 
 
@@ -43,7 +49,7 @@ def test_pairs_u32_sizes_full_range(n):
 
 
 @pytest.mark.parametrize("b,e", RANGES)
-@pytest.mark.parametrize("n", [65, TILE + 1, 5 * TILE - 3])
+@pytest.mark.parametrize("n", [65, 3000, TILE + 1, 5 * TILE - 3, LARGE + 2 * TILE + 5])
 def test_pairs_u32_bit_ranges(n, b, e):
     print("pairs u32 n=%d bits=[%d,%d)" % (n, b, e), flush=True)
     check_pairs(rng(n + b * 33 + e).integers(0, 2**32, n, dtype=np.uint32), b, e)
@@ -51,8 +57,8 @@ def test_pairs_u32_bit_ranges(n, b, e):
 
 @pytest.mark.parametrize("kind", ["all_equal", "all_max", "single_digit", "few_values",
                                   "sorted", "reversed", "zipf", "top_byte_only"])
-def test_pairs_u32_distributions(kind):
-    n = 3 * TILE + 1234
+@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE + 1234])
+def test_pairs_u32_distributions(kind, n):
     r = rng(11)
     if kind == "all_equal":
         keys = np.full(n, 0x12345678, np.uint32)
@@ -70,12 +76,13 @@ def test_pairs_u32_distributions(kind):
         keys = workloads.zipf_u32(n, seed=3)
     else:
         keys = r.integers(0, 256, n, dtype=np.uint32) << np.uint32(24)
-    print("pairs u32 distribution=%s" % kind, flush=True)
+    print("pairs u32 distribution=%s n=%d" % (kind, n), flush=True)
     for (b, e) in [(0, 32), (0, 16), (16, 32)]:
         check_pairs(keys, b, e)
 
 
-@pytest.mark.parametrize("n", [1, 64, 1000, TILE + 1, 3 * TILE + 17, (1 << 20) + 17])
+@pytest.mark.parametrize("n", [1, 64, 1000, 4000, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17,
+                               LARGE + 17])
 @pytest.mark.parametrize("b,e", [(0, 32), (4, 13), (8, 24)])
 def test_keys_u32(n, b, e):
     print("keys u32 n=%d bits=[%d,%d)" % (n, b, e), flush=True)
@@ -85,7 +92,8 @@ def test_keys_u32(n, b, e):
     assert np.array_equal(k, oracle.sort_u32(keys, None, b, e))
 
 
-@pytest.mark.parametrize("n", [1, 65, 1000, TILE + 1, 3 * TILE + 17, (1 << 20) + 17])
+@pytest.mark.parametrize("n", [1, 65, 1000, 4000, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17,
+                               LARGE + 17])
 @pytest.mark.parametrize("b,e", [(0, 32), (0, 16), (16, 32), (3, 29), (31, 32)])
 def test_pairs_f32(n, b, e):
     print("pairs f32 n=%d bits=[%d,%d)" % (n, b, e), flush=True)
@@ -153,9 +161,10 @@ def test_bitonic_bit_ranges(b, e):
     assert np.array_equal(gpu_bitonic(keys, 1000, b, e), oracle.bitonic_tile(keys, 1000, b, e))
 
 
-def test_back_to_back_calls_share_temp():
+@pytest.mark.parametrize("n", [4 * TILE + 99, LARGE + 99])
+def test_back_to_back_calls_share_temp(n):
     """Stale counters or tile states from an earlier call must not leak."""
-    n = 4 * TILE + 99
+    print("back-to-back n=%d" % n, flush=True)
     need = 0
     import sorting_lsd_radix_amd as rs
     need = rs.rs_sort_pairs_u32(None, None, None, None, n, 0, 32, None, 0)
@@ -175,7 +184,7 @@ def test_back_to_back_calls_share_temp():
 # --- the named workloads, at their full sizes ------------------------------------------
 
 def test_workload_tile_1024_keys():
-    """1024 uniform keys: both the bitonic tile and the 4-pass radix path."""
+    """1024 uniform keys: both the bitonic tile and the 4-pass radix sort (in one workgroup)."""
     keys = workloads.tile_keys()
     ref = oracle.sort_u32(keys)
     assert np.array_equal(gpu_bitonic(keys, 1024), ref)
