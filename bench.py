@@ -7,6 +7,7 @@ inputs, outputs and temp already resident in HBM.  Prints one JSON line.
 
   python bench.py [--gpus 1] [--steps K] [--warmup W] [--workload NAME | --all]
                   [--no-cpu-baseline] [--no-check] [--copy-calibration]
+  python bench.py --workload NAME --record-traffic FETCH_DIR WRITE_DIR
 
 The roofline entry is for the dominant kernel of the workload (the one-sweep
 pass for sorts, the one-workgroup tile sort for sorts of at most 16384 keys,
@@ -276,6 +277,63 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
     return result
 
 
+KERNEL_MATCH = {"onesweep": "onesweep_kernel", "upsweep": "upsweep_kernel",
+                "compact": "compact_kernel", "tile_sort": "tile_sort_kernel",
+                "bitonic": "bitonic_tile_kernel", "copy": "__amd_rocclr_copyBuffer"}
+COPY_BYTES = 4 << 28   # the --copy-calibration copy moves 1 GiB each way
+
+
+def record_traffic(name, fetch_dir, write_dir):
+    """Per-launch HBM bytes of the workload's dominant kernel from two
+    rocprofv3 --pmc runs (FETCH_SIZE, then WRITE_SIZE, both with
+    --copy-calibration), each counter scaled by what it reads for the 1 GiB
+    device copy of the same run; written to profiles/traffic.json."""
+    import csv
+
+    def per_kernel(d):
+        out = {}
+        with open(os.path.join(d, "run_counter_collection.csv")) as f:
+            for r in csv.DictReader(f):
+                for k, pat in KERNEL_MATCH.items():
+                    if pat in r["Kernel_Name"]:
+                        out.setdefault(k, []).append(float(r["Counter_Value"]))
+        return {k: sum(v) / len(v) for k, v in out.items()}
+
+    fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
+    desc, kind, n, b, e = WORKLOADS[name]
+    dom = ("compact" if kind == "compact" else "bitonic" if kind == "bitonic"
+           else "tile_sort" if n <= TILE_SORT_MAX else "onesweep")
+    bytes_per = 8 if kind in ("keys_u32", "compact", "bitonic") else 16
+    f_factor = COPY_BYTES / (fetch["copy"] * 1024)
+    w_factor = COPY_BYTES / (write["copy"] * 1024)
+    entry = {
+        "source_sha": source_hash(),
+        "kernel": dom,
+        "traffic_bytes_per_launch": round(fetch[dom] * 1024 * f_factor + write[dom] * 1024 * w_factor),
+        "fetch_bytes_per_launch": round(fetch[dom] * 1024 * f_factor),
+        "write_bytes_per_launch": round(write[dom] * 1024 * w_factor),
+        "algorithmic_bytes_per_launch": bytes_per * n,
+        "calibration": {"copy_bytes_each_way": COPY_BYTES, "fetch_size_kib": round(fetch["copy"], 1),
+                        "write_size_kib": round(write["copy"], 1), "fetch_factor": round(f_factor, 4),
+                        "write_factor": round(w_factor, 4)},
+        "commands": ["rocprofv3 --pmc %s --output-format csv -d %s -o run -- python3 bench.py --workload %s "
+                     "--steps 2 --warmup 1 --no-cpu-baseline --no-check --copy-calibration" % (c, d, name)
+                     for c, d in (("FETCH_SIZE", fetch_dir), ("WRITE_SIZE", write_dir))],
+    }
+    if "upsweep" in fetch:
+        entry["upsweep_fetch_bytes_per_launch"] = round(fetch["upsweep"] * 1024 * f_factor)
+        entry["upsweep_write_bytes_per_launch"] = round(write["upsweep"] * 1024 * w_factor)
+    table = {}
+    if os.path.exists(TRAFFIC_FILE):
+        with open(TRAFFIC_FILE) as f:
+            table = json.load(f)
+    table[name] = entry
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(table, f, indent=2)
+        f.write("\n")
+    print(json.dumps({name: entry}))
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -287,8 +345,14 @@ def main():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
+                    help="write profiles/traffic.json for --workload from two rocprofv3 --pmc "
+                         "output folders (FETCH_SIZE, WRITE_SIZE) and exit; no GPU needed")
     args = ap.parse_args()
 
+    if args.record_traffic:
+        record_traffic(args.workload, *args.record_traffic)
+        return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
               "(--gpus %d requested)" % args.gpus, file=sys.stderr)

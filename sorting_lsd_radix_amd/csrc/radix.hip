@@ -170,46 +170,31 @@ struct PassArgs {
     const uint32_t* bins;      // global digit counts of this pass
     uint32_t* states;          // look-back words of this pass, zeroed
     uint32_t* next_states;     // look-back words of the next pass, cleared here (or null)
-    uint32_t* sched;           // tile scheduler of this pass, zeroed
-    uint32_t max_chunks;       // chunk-map entries per XCD group
+    uint32_t* sched;           // tile counters of this pass (one per group), zeroed
+    uint32_t groups;           // block groups = min(8, grid)
     uint32_t chunk_log2;       // tiles per chunk = 2^chunk_log2 (at most the blocks per group)
 };
 
-// Index of the XCD (accelerator complex die) this wave runs on.
-__device__ __forceinline__ uint32_t xcd_id() {
-    return static_cast<uint32_t>(__builtin_amdgcn_s_getreg((3 << 11) | (0 << 6) | 20)) & 0xFu;
-}
-
-// Tile scheduler.  Tiles are handed out in chunks of 2^chunk_log2 consecutive
-// tiles; each XCD group works through one chunk at a time, so neighbouring
-// tiles run on the same XCD and the cache lines their digit runs share are
-// merged in that XCD's L2 before they reach memory.  Chunks go to whichever
-// group needs one next, from one global counter, which keeps the tiles in
-// flight close together in index order (short look-backs) and lets a faster
-// XCD take more chunks.  A chunk is no larger than the blocks of a group, so
-// a group runs all tiles of its chunk at once, and a block starts every tile
-// it takes at once.  The smallest unfinished tile is therefore either running
-// (every earlier tile is done, so its look-back ends) or not yet handed out,
-// and then a block is free to take it, so look-back always makes progress.
-// Layout: sched[0] global chunk counter, sched[1 + g] tiles taken by group g,
-// sched[16 + g * max_chunks + j] = 1 + global index of group g's j-th chunk.
-__device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t max_chunks,
+// Tile scheduler.  Block b belongs to group b mod groups (groups = min(8,
+// grid)); workgroups are dispatched round-robin over the 8 XCDs, so with 8
+// groups a group is the set of blocks on one XCD.  The tiles form chunks of
+// 2^chunk_log2 consecutive tiles, and group g owns the chunks g, g + groups,
+// g + 2 groups, ...; its blocks take that sequence in order from one counter.
+// Neighbouring tiles thus run at the same time on one XCD, and the cache
+// lines their digit runs share are merged in that XCD's L2 before they reach
+// memory.  A block starts each tile it takes at once, every group has a
+// block, and a group hands out its tiles in increasing order.  So the
+// smallest unfinished tile is either running (every earlier tile is done,
+// and its look-back ends) or not yet handed out, and then every tile its
+// group has handed out is smaller, hence done, and a block of that group is
+// free to take it: look-back always makes progress.
+// Layout: sched[g] = tiles taken by group g.
+__device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t groups,
                                               uint32_t chunk_log2, uint32_t group,
                                               uint32_t tiles) {
-    const uint32_t k = fetch_add_agent(&sched[1 + group], 1u);
-    const uint32_t j = k >> chunk_log2, off = k & ((1u << chunk_log2) - 1u);
-    if (j >= max_chunks) return tiles;   // never reached: max_chunks covers every taker
-    uint32_t* slot = &sched[16 + group * max_chunks + j];
-    uint32_t c;
-    if (off == 0) {
-        c = fetch_add_agent(&sched[0], 1u);
-        store_state(slot, c + 1u);
-    } else {
-        uint32_t v;
-        while ((v = load_state(slot)) == 0u) __builtin_amdgcn_s_sleep(1);
-        c = v - 1u;
-    }
-    const uint64_t t = (static_cast<uint64_t>(c) << chunk_log2) + off;
+    const uint32_t k = fetch_add_agent(&sched[group], 1u);
+    const uint64_t chunk = static_cast<uint64_t>(k >> chunk_log2) * groups + group;
+    const uint64_t t = (chunk << chunk_log2) | (k & ((1u << chunk_log2) - 1u));
     return t < tiles ? static_cast<uint32_t>(t) : tiles;
 }
 
@@ -263,7 +248,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     uint32_t* __restrict__ states = a.states;
     const uint32_t n = a.n, shift = a.shift, width = a.width, tiles = a.tiles;
     const uint32_t last_digit = (1u << width) - 1u;
-    const uint32_t group = xcd_id() % kGroups;
+    const uint32_t group = blockIdx.x % a.groups;
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
@@ -272,7 +257,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
         // A tile is taken only when the block can start on it at once: the
         // time from taking a tile to publishing its count delays every later
         // tile's look-back.
-        if (tid == 0) s_next = next_tile(a.sched, a.max_chunks, a.chunk_log2, group, tiles);
+        if (tid == 0) s_next = next_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
         // Only this wave reads and writes its counters during the rank, and the
         // previous tile's readers of s_off all passed a barrier since.
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
@@ -597,7 +582,7 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
 
 // Temp layout (every piece 256-byte aligned):
 //   bins     [kMaxPasses][256] u32   global digit counts of each pass
-//   sched    [kMaxPasses][sched_words] u32   tile schedulers (see next_tile)
+//   sched    [kMaxPasses][64]  u32   tile counters of each pass, one per group (see next_tile)
 //   states0  [tiles][256]      u32   look-back states of even passes
 //   states1  [tiles][256]      u32   look-back states of odd passes (passes >= 2)
 //   tmp_keys [n] u32, tmp_vals [n] u32   ping-pong buffers (passes >= 2)
@@ -605,24 +590,21 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
 struct SortLayout {
     size_t bins, sched, states0, states1, tmp_keys, tmp_vals, total;
     uint64_t clear_words;
-    uint32_t tiles, max_chunks, sched_words;
+    uint32_t tiles;
 };
 
-// Upper bound of the blocks one pass keeps resident (sizes the chunk map).
-constexpr uint32_t kMaxResidentBlocks = 4096;
+constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
+constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
 SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
     SortLayout L{};
     L.tiles = static_cast<uint32_t>((n + kSortTile - 1) / kSortTile);
-    // a group takes at most tiles + (its blocks) chunk slots, whatever the chunk size
-    L.max_chunks = L.tiles + kMaxResidentBlocks + 2;
-    L.sched_words = static_cast<uint32_t>(align_up((16 + kGroups * L.max_chunks) * 4) / 4);
     const size_t states_bytes = align_up(static_cast<size_t>(L.tiles) * kRadix * 4);
     size_t off = 0;
     L.bins = off;
     off += align_up(kMaxPasses * kRadix * 4);
     L.sched = off;
-    off += static_cast<size_t>(kMaxPasses) * L.sched_words * 4;
+    off += static_cast<size_t>(kMaxPasses) * kSchedWords * 4;
     L.states0 = off;
     off += states_bytes;
     L.clear_words = off / 4;
@@ -666,9 +648,11 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     if (resident == 0) resident = resident_blocks(kern, BLOCK);
     const uint32_t grid = a.tiles < resident ? a.tiles : resident;
     PassArgs b = a;
-    // chunk: the largest power of two not above the blocks per group, capped
+    // every group needs a block; a chunk is the largest power of two not above
+    // the blocks per group, capped
+    b.groups = grid < static_cast<uint32_t>(kGroups) ? grid : static_cast<uint32_t>(kGroups);
     b.chunk_log2 = 0;
-    while ((2u << b.chunk_log2) <= grid / kGroups && (2u << b.chunk_log2) <= kChunk) ++b.chunk_log2;
+    while ((2u << b.chunk_log2) <= grid / b.groups && (2u << b.chunk_log2) <= kChunk) ++b.chunk_log2;
     kern<<<dim3(grid), BLOCK, 0, s>>>(b);
     return hipGetLastError();
 }
@@ -792,8 +776,7 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
         a.bins = bins + p * kRadix;
         a.states = states[p & 1];
         a.next_states = (p + 1 < passes) ? states[(p + 1) & 1] : nullptr;
-        a.sched = sched + static_cast<size_t>(p) * L.sched_words;
-        a.max_chunks = L.max_chunks;
+        a.sched = sched + static_cast<size_t>(p) * kSchedWords;
         const bool flip_in = is_f32 && p == 0;
         const bool flip_out = is_f32 && p == passes - 1;
         timing_before(stream, RS_KERNEL_ONESWEEP);
