@@ -32,8 +32,13 @@ namespace {
 constexpr int kSortBlock = 1024;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
+// A keys-only pass has registers for twice the keys per thread (no values),
+// and a 32768-key tile halves its per-tile work (scans, look-back, tile
+// hand-out) per key; it is used once there is a tile for every CU.
+constexpr int kKeysItems = 32;
+constexpr uint64_t kKeysLargeMinN = 256ull * kSortBlock * kKeysItems;
 // Up to this many keys the whole sort runs in one block, in LDS.
-constexpr uint32_t kTileSortMax = kSortTile;
+constexpr uint32_t kTileSortMax = 16384;
 constexpr int kSortLookback = 8;       // earlier tiles read per look-back batch
 constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
 constexpr int kGroups = 8;             // XCDs
@@ -596,9 +601,16 @@ struct SortLayout {
 constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
 constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
+// Keys per tile of the one-sweep pass.
+uint64_t pass_tile_keys(uint64_t n, bool pairs) {
+    return (!pairs && n >= kKeysLargeMinN) ? static_cast<uint64_t>(kSortBlock) * kKeysItems
+                                           : static_cast<uint64_t>(kSortTile);
+}
+
 SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
     SortLayout L{};
-    L.tiles = static_cast<uint32_t>((n + kSortTile - 1) / kSortTile);
+    const uint64_t tile_keys = pass_tile_keys(n, pairs);
+    L.tiles = static_cast<uint32_t>((n + tile_keys - 1) / tile_keys);
     const size_t states_bytes = align_up(static_cast<size_t>(L.tiles) * kRadix * 4);
     size_t off = 0;
     L.bins = off;
@@ -657,12 +669,19 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
+template <int ITEMS, bool PAIRS>
+hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
+    if (flip_in && flip_out) return launch_pass_t<kSortBlock, ITEMS, PAIRS, true, true>(a, s);
+    if (flip_in) return launch_pass_t<kSortBlock, ITEMS, PAIRS, true, false>(a, s);
+    if (flip_out) return launch_pass_t<kSortBlock, ITEMS, PAIRS, false, true>(a, s);
+    return launch_pass_t<kSortBlock, ITEMS, PAIRS, false, false>(a, s);
+}
+
 template <bool PAIRS>
 hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (flip_in && flip_out) return launch_pass_t<kSortBlock, kSortItems, PAIRS, true, true>(a, s);
-    if (flip_in) return launch_pass_t<kSortBlock, kSortItems, PAIRS, true, false>(a, s);
-    if (flip_out) return launch_pass_t<kSortBlock, kSortItems, PAIRS, false, true>(a, s);
-    return launch_pass_t<kSortBlock, kSortItems, PAIRS, false, false>(a, s);
+    if (!PAIRS && pass_tile_keys(a.n, false) != static_cast<uint64_t>(kSortTile))
+        return launch_pass_items<kKeysItems, false>(flip_in, flip_out, a, s);
+    return launch_pass_items<kSortItems, PAIRS>(flip_in, flip_out, a, s);
 }
 
 template <int BLOCK, int ITEMS, bool PAIRS>
@@ -683,7 +702,7 @@ void launch_tile_sort(const uint32_t* ki, uint32_t* ko, const uint32_t* vi, uint
     else if (n <= 512 * 8)
         launch_tile_sort_t<512, 8, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
     else
-        launch_tile_sort_t<kSortBlock, kSortItems, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+        launch_tile_sort_t<1024, 16, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
 }
 
 int upsweep_grid(uint32_t n) {

@@ -24,6 +24,7 @@ pytestmark = pytest.mark.gpu
 TILE = 16384
 STILE = 4096
 LARGE = 256 * TILE
+KLARGE = 256 * 2 * TILE  # keys-only sorts use 32768-key tiles from here on
 CTILE = 32768  # floats per tile of the compaction
 SIZES = [1, 2, 63, 64, 65, 1000, 1024, 1025, STILE, STILE + 1, TILE - 1, TILE, TILE + 1,
          3 * TILE + 17, (1 << 20) + 17, LARGE - 1, LARGE, LARGE + 17]
@@ -82,7 +83,7 @@ def test_pairs_u32_distributions(kind, n):
 
 
 @pytest.mark.parametrize("n", [1, 64, 1000, 4000, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17,
-                               LARGE + 17])
+                               LARGE + 17, KLARGE - 1, KLARGE, KLARGE + 2 * TILE + 17])
 @pytest.mark.parametrize("b,e", [(0, 32), (4, 13), (8, 24)])
 def test_keys_u32(n, b, e):
     print("keys u32 n=%d bits=[%d,%d)" % (n, b, e), flush=True)
