@@ -12,6 +12,8 @@ constexpr int kWave = 64;          // CDNA wavefront width
 // 16-byte vector of u32 (a clang vector type, usable with the nontemporal builtins)
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 constexpr int kRadixBits = 8;      // digit width of every sort pass
+// Word 3 of a raw buffer descriptor on gfx9-family chips (32-bit data format).
+constexpr int kBufferWord3 = 0x00020000;
 constexpr int kRadix = 1 << kRadixBits;
 
 // Cross-tile state word: 2 status bits over a 30-bit count.
@@ -45,6 +47,29 @@ __device__ __forceinline__ void store_state(uint32_t* p, uint32_t v) {
 
 __device__ __forceinline__ uint32_t fetch_add_agent(uint32_t* p, uint32_t v) {
     return __hip_atomic_fetch_add(p, v, __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_AGENT);
+}
+
+// Tile scheduler of the persistent tile kernels (sort passes, compaction).
+// Block b belongs to group b mod groups (groups = min(8, grid)); workgroups
+// are dispatched round-robin over the 8 XCDs, so with 8 groups a group is the
+// set of blocks on one XCD.  The tiles form chunks of 2^chunk_log2
+// consecutive tiles, and group g owns the chunks g, g + groups, g + 2 groups,
+// ...; its blocks take that sequence in order from one counter.  Neighbouring
+// tiles thus run at the same time on one XCD, and the cache lines their
+// output runs share are merged in that XCD's L2 before they reach memory.  A block starts each tile it takes at once, every group has a
+// block, and a group hands out its tiles in increasing order.  So the
+// smallest unfinished tile is either running (every earlier tile is done,
+// and its look-back ends) or not yet handed out, and then every tile its
+// group has handed out is smaller, hence done, and a block of that group is
+// free to take it: look-back always makes progress.
+// Layout: sched[g] = tiles taken by group g.
+__device__ __forceinline__ uint32_t next_chunked_tile(uint32_t* sched, uint32_t groups,
+                                                      uint32_t chunk_log2, uint32_t group,
+                                                      uint32_t tiles) {
+    const uint32_t k = fetch_add_agent(&sched[group], 1u);
+    const uint64_t chunk = static_cast<uint64_t>(k >> chunk_log2) * groups + group;
+    const uint64_t t = (chunk << chunk_log2) | (k & ((1u << chunk_log2) - 1u));
+    return t < tiles ? static_cast<uint32_t>(t) : tiles;
 }
 
 // Order-preserving transform of binary32 patterns: flips every bit of a

@@ -14,6 +14,18 @@ namespace rs {
 void timing_before(hipStream_t s, int kernel_id);
 void timing_after(hipStream_t s);
 
+// ---- persistent tile kernels ----------------------------------------------------
+
+// Compute units of the current device (cached).
+int device_cus();
+
+// Launch shape of a persistent tile kernel: grid (at most `resident` blocks),
+// block groups (one per XCD) and tiles per chunk (see next_chunked_tile).
+struct TileGrid {
+    uint32_t grid, groups, chunk_log2;
+};
+TileGrid tile_grid(uint32_t tiles, uint32_t resident);
+
 // ---- radix sort ---------------------------------------------------------------
 
 // Temp bytes for a sort of n keys with `passes` 8-bit passes.

@@ -42,8 +42,8 @@ constexpr uint32_t kTileSortMax = 16384;
 constexpr int kSortLookback = 8;       // earlier tiles read per look-back batch
 constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
 constexpr int kGroups = 8;             // XCDs
-// Word 3 of a raw buffer descriptor on gfx9-family chips (32-bit data format).
-constexpr int kBufferWord3 = 0x00020000;
+// Cache-policy operand of a buffer access: the non-temporal bit.
+constexpr int kNonTemporal = 2;
 
 constexpr int kUpBlock = 256;
 constexpr int kUpSub = 8;          // sub-histograms per digit (spreads LDS atomics)
@@ -180,49 +180,23 @@ struct PassArgs {
     uint32_t chunk_log2;       // tiles per chunk = 2^chunk_log2 (at most the blocks per group)
 };
 
-// Tile scheduler.  Block b belongs to group b mod groups (groups = min(8,
-// grid)); workgroups are dispatched round-robin over the 8 XCDs, so with 8
-// groups a group is the set of blocks on one XCD.  The tiles form chunks of
-// 2^chunk_log2 consecutive tiles, and group g owns the chunks g, g + groups,
-// g + 2 groups, ...; its blocks take that sequence in order from one counter.
-// Neighbouring tiles thus run at the same time on one XCD, and the cache
-// lines their digit runs share are merged in that XCD's L2 before they reach
-// memory.  A block starts each tile it takes at once, every group has a
-// block, and a group hands out its tiles in increasing order.  So the
-// smallest unfinished tile is either running (every earlier tile is done,
-// and its look-back ends) or not yet handed out, and then every tile its
-// group has handed out is smaller, hence done, and a block of that group is
-// free to take it: look-back always makes progress.
-// Layout: sched[g] = tiles taken by group g.
-__device__ __forceinline__ uint32_t next_tile(uint32_t* sched, uint32_t groups,
-                                              uint32_t chunk_log2, uint32_t group,
-                                              uint32_t tiles) {
-    const uint32_t k = fetch_add_agent(&sched[group], 1u);
-    const uint64_t chunk = static_cast<uint64_t>(k >> chunk_log2) * groups + group;
-    const uint64_t t = (chunk << chunk_log2) | (k & ((1u << chunk_log2) - 1u));
-    return t < tiles ? static_cast<uint32_t>(t) : tiles;
-}
-
 // Loads the ITEMS keys of this lane for `tile`: row j of wave w is the 64
-// consecutive keys at tile*TILE + w*64*ITEMS + j*64.  Partial tiles read only
-// in-range addresses (clamped); the padding is applied after the flip.
+// consecutive keys at tile*TILE + w*64*ITEMS + j*64.  The loads go through a
+// buffer descriptor of n elements, so a row past the end of a partial tile
+// reads 0 without a branch or a clamp (the padding is applied afterwards);
+// they are non-temporal, since each key is read once per pass.  The row
+// offsets fold into the instructions' immediate offsets.
 template <int ITEMS, int TILE>
 __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint32_t tile,
                                           uint32_t n, uint32_t wave, uint32_t lane,
                                           uint32_t (&x)[ITEMS]) {
-    const uint32_t first = tile * TILE + wave * (kWave * ITEMS) + lane;
-    if (tile * TILE + TILE <= n) {
-        // row offsets fold into the load; non-temporal: each key is read once per pass
-        const uint32_t* p = src + first;
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(src), 0, static_cast<int>(n * 4u), kBufferWord3);
+    const uint32_t first = (tile * TILE + wave * (kWave * ITEMS) + lane) * 4u;
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) x[j] = __builtin_nontemporal_load(&p[j * kWave]);
-    } else {
-#pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t idx = first + j * kWave;
-            x[j] = src[idx < n ? idx : n - 1];
-        }
-    }
+    for (int j = 0; j < ITEMS; ++j)
+        x[j] = __builtin_amdgcn_raw_buffer_load_b32(r, static_cast<int>(first + j * kWave * 4), 0,
+                                                    kNonTemporal);
 }
 
 // One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
@@ -262,7 +236,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
         // A tile is taken only when the block can start on it at once: the
         // time from taking a tile to publishing its count delays every later
         // tile's look-back.
-        if (tid == 0) s_next = next_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
+        if (tid == 0) s_next = next_chunked_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
         // Only this wave reads and writes its counters during the rank, and the
         // previous tile's readers of s_off all passed a barrier since.
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
@@ -587,7 +561,7 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
 
 // Temp layout (every piece 256-byte aligned):
 //   bins     [kMaxPasses][256] u32   global digit counts of each pass
-//   sched    [kMaxPasses][64]  u32   tile counters of each pass, one per group (see next_tile)
+//   sched    [kMaxPasses][64]  u32   tile counters of each pass, one per group (next_chunked_tile)
 //   states0  [tiles][256]      u32   look-back states of even passes
 //   states1  [tiles][256]      u32   look-back states of odd passes (passes >= 2)
 //   tmp_keys [n] u32, tmp_vals [n] u32   ping-pong buffers (passes >= 2)
@@ -630,18 +604,6 @@ SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
     return L;
 }
 
-int device_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
-        if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
-    return cus;
-}
-
 // Resident blocks of one pass kernel instance (occupancy x CUs), cached.
 template <typename K>
 uint32_t resident_blocks(K kernel, int block) {
@@ -658,14 +620,11 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     static uint32_t resident = 0;
     auto kern = onesweep_kernel<BLOCK, ITEMS, kSortLookback, PAIRS, FI, FO>;
     if (resident == 0) resident = resident_blocks(kern, BLOCK);
-    const uint32_t grid = a.tiles < resident ? a.tiles : resident;
+    const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
-    // every group needs a block; a chunk is the largest power of two not above
-    // the blocks per group, capped
-    b.groups = grid < static_cast<uint32_t>(kGroups) ? grid : static_cast<uint32_t>(kGroups);
-    b.chunk_log2 = 0;
-    while ((2u << b.chunk_log2) <= grid / b.groups && (2u << b.chunk_log2) <= kChunk) ++b.chunk_log2;
-    kern<<<dim3(grid), BLOCK, 0, s>>>(b);
+    b.groups = g.groups;
+    b.chunk_log2 = g.chunk_log2;
+    kern<<<dim3(g.grid), BLOCK, 0, s>>>(b);
     return hipGetLastError();
 }
 
@@ -715,6 +674,30 @@ int upsweep_grid(uint32_t n) {
 }
 
 }  // namespace
+
+TileGrid tile_grid(uint32_t tiles, uint32_t resident) {
+    TileGrid g{};
+    g.grid = tiles < resident ? tiles : resident;
+    if (g.grid == 0) g.grid = 1;
+    // every group needs a block; a chunk is the largest power of two not above
+    // the blocks per group, capped
+    g.groups = g.grid < static_cast<uint32_t>(kGroups) ? g.grid : static_cast<uint32_t>(kGroups);
+    g.chunk_log2 = 0;
+    while ((2u << g.chunk_log2) <= g.grid / g.groups && (2u << g.chunk_log2) <= kChunk) ++g.chunk_log2;
+    return g;
+}
+
+int device_cus() {
+    static int cus = 0;
+    if (cus == 0) {
+        int dev = 0;
+        if (hipGetDevice(&dev) != hipSuccess ||
+            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            cus <= 0)
+            cus = 256;
+    }
+    return cus;
+}
 
 size_t sort_temp_bytes(uint64_t n, bool pairs, int passes) {
     if (n <= kTileSortMax) return kAlign;   // the one-block sort needs no temp storage
