@@ -37,6 +37,11 @@ constexpr int kSortTile = kSortBlock * kSortItems;
 // hand-out) per key; it is used once there is a tile for every CU.
 constexpr int kKeysItems = 32;
 constexpr uint64_t kKeysLargeMinN = 256ull * kSortBlock * kKeysItems;
+// A pair pass fits 24 keys and values per thread in registers (28 spills,
+// 32 spills heavily); the 24576-key tile is used once there is a tile for
+// every CU.
+constexpr int kPairsItems = 24;
+constexpr uint64_t kPairsLargeMinN = 256ull * kSortBlock * kPairsItems;
 // Up to this many keys the whole sort runs in one block, in LDS.
 constexpr uint32_t kTileSortMax = 16384;
 constexpr int kSortLookback = 2;       // earlier tiles read per look-back batch (a wave waits for
@@ -209,7 +214,7 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
     constexpr int TILE = BLOCK * ITEMS;
     constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
-    static_assert((TILE & (TILE - 1)) == 0 && TILE <= 32768, "tile: a power of two, 16-bit positions");
+    static_assert(TILE <= 32768, "16-bit positions");
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
 
     // One staging buffer: the keys in digit order, then the values in digit order.
@@ -351,9 +356,10 @@ __global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
             uint32_t key = k[j];
             asm volatile("" : "+v"(key));
             const uint32_t d = __builtin_amdgcn_ubfe(key, shift, width);
-            // (the mask never changes a consistent position; it keeps the store in the tile)
+            // (the clamp never changes a consistent position; it keeps the store in the tile)
             const uint32_t sh = 16 * (j % 2);
-            const uint32_t p = (s_off[wave * kRadix + d] + ((pos[j / 2] >> sh) & 0xFFFFu)) & (TILE - 1);
+            const uint32_t p = min(s_off[wave * kRadix + d] + ((pos[j / 2] >> sh) & 0xFFFFu),
+                                   static_cast<uint32_t>(TILE - 1));
             pos[j / 2] = (pos[j / 2] & ~(0xFFFFu << sh)) | (p << sh);
             s_buf[p] = key;
         }
@@ -579,8 +585,9 @@ constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
 // Keys per tile of the one-sweep pass.
 uint64_t pass_tile_keys(uint64_t n, bool pairs) {
-    return (!pairs && n >= kKeysLargeMinN) ? static_cast<uint64_t>(kSortBlock) * kKeysItems
-                                           : static_cast<uint64_t>(kSortTile);
+    if (pairs && n >= kPairsLargeMinN) return static_cast<uint64_t>(kSortBlock) * kPairsItems;
+    if (!pairs && n >= kKeysLargeMinN) return static_cast<uint64_t>(kSortBlock) * kKeysItems;
+    return static_cast<uint64_t>(kSortTile);
 }
 
 SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
@@ -640,8 +647,8 @@ hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hip
 
 template <bool PAIRS>
 hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (!PAIRS && pass_tile_keys(a.n, false) != static_cast<uint64_t>(kSortTile))
-        return launch_pass_items<kKeysItems, false>(flip_in, flip_out, a, s);
+    if (pass_tile_keys(a.n, PAIRS) != static_cast<uint64_t>(kSortTile))
+        return launch_pass_items<PAIRS ? kPairsItems : kKeysItems, PAIRS>(flip_in, flip_out, a, s);
     return launch_pass_items<kSortItems, PAIRS>(flip_in, flip_out, a, s);
 }
 

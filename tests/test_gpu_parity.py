@@ -20,14 +20,18 @@ pytestmark = pytest.mark.gpu
 
 # Sort paths: up to TILE keys one workgroup sorts in LDS (tile shapes of 1024,
 # 4096 and 16384 keys); above, the one-sweep passes use TILE-key tiles.  LARGE
-# is the first size at which every CU gets a tile.
+# is the first size at which every CU gets a tile; pair sorts switch to
+# PTILE-key tiles at PLARGE and keys-only sorts to 32768-key tiles at KLARGE.
 TILE = 16384
 STILE = 4096
 LARGE = 256 * TILE
 KLARGE = 256 * 2 * TILE  # keys-only sorts use 32768-key tiles from here on
+PTILE = 24576  # keys per tile of a pair sort from PLARGE on
+PLARGE = 256 * PTILE
 CTILE = 32768  # floats per tile of the compaction
 SIZES = [1, 2, 63, 64, 65, 1000, 1024, 1025, STILE, STILE + 1, TILE - 1, TILE, TILE + 1,
-         3 * TILE + 17, (1 << 20) + 17, LARGE - 1, LARGE, LARGE + 17]
+         3 * TILE + 17, (1 << 20) + 17, LARGE - 1, LARGE, LARGE + 17, PLARGE - 1, PLARGE,
+         PLARGE + 2 * PTILE + 17]
 RANGES = [(0, 32), (0, 16), (8, 24), (4, 13), (0, 1), (31, 32), (7, 7), (0, 8), (24, 32)]
 
 
@@ -50,7 +54,8 @@ def test_pairs_u32_sizes_full_range(n):
 
 
 @pytest.mark.parametrize("b,e", RANGES)
-@pytest.mark.parametrize("n", [65, 3000, TILE + 1, 5 * TILE - 3, LARGE + 2 * TILE + 5])
+@pytest.mark.parametrize("n", [65, 3000, TILE + 1, 5 * TILE - 3, LARGE + 2 * TILE + 5,
+                               PLARGE + 3 * PTILE + 5])
 def test_pairs_u32_bit_ranges(n, b, e):
     print("pairs u32 n=%d bits=[%d,%d)" % (n, b, e), flush=True)
     check_pairs(rng(n + b * 33 + e).integers(0, 2**32, n, dtype=np.uint32), b, e)
@@ -58,7 +63,7 @@ def test_pairs_u32_bit_ranges(n, b, e):
 
 @pytest.mark.parametrize("kind", ["all_equal", "all_max", "single_digit", "few_values",
                                   "sorted", "reversed", "zipf", "top_byte_only"])
-@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE + 1234])
+@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE + 1234, PLARGE + 1234])
 def test_pairs_u32_distributions(kind, n):
     r = rng(11)
     if kind == "all_equal":
@@ -94,7 +99,7 @@ def test_keys_u32(n, b, e):
 
 
 @pytest.mark.parametrize("n", [1, 65, 1000, 4000, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17,
-                               LARGE + 17])
+                               LARGE + 17, PLARGE + 17])
 @pytest.mark.parametrize("b,e", [(0, 32), (0, 16), (16, 32), (3, 29), (31, 32)])
 def test_pairs_f32(n, b, e):
     print("pairs f32 n=%d bits=[%d,%d)" % (n, b, e), flush=True)
@@ -162,7 +167,7 @@ def test_bitonic_bit_ranges(b, e):
     assert np.array_equal(gpu_bitonic(keys, 1000, b, e), oracle.bitonic_tile(keys, 1000, b, e))
 
 
-@pytest.mark.parametrize("n", [4 * TILE + 99, LARGE + 99])
+@pytest.mark.parametrize("n", [4 * TILE + 99, LARGE + 99, PLARGE + 99])
 def test_back_to_back_calls_share_temp(n):
     """Stale counters or tile states from an earlier call must not leak."""
     print("back-to-back n=%d" % n, flush=True)
