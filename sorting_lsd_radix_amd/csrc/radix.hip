@@ -29,19 +29,26 @@ namespace rs {
 
 namespace {
 
+// Shapes of the one-sweep pass (threads per block x keys per thread).
+// Every shape allows 4 waves per SIMD, i.e. 128 registers per lane: one
+// 1024-thread block or two 512-thread blocks per CU.
+constexpr int kPassWavesPerSimd = 4;
+// Small sorts: 1024 x 16.
 constexpr int kSortBlock = 1024;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
-// A keys-only pass has registers for twice the keys per thread (no values),
-// and a 32768-key tile halves its per-tile work (scans, look-back, tile
-// hand-out) per key; it is used once there is a tile for every CU.
-constexpr int kKeysItems = 32;
-constexpr uint64_t kKeysLargeMinN = 256ull * kSortBlock * kKeysItems;
-// A pair pass fits 24 keys and values per thread in registers (28 spills,
-// 32 spills heavily); the 24576-key tile is used once there is a tile for
-// every CU.
+// Large pair sorts: 24 keys and values per thread still fit the registers
+// (28 spills), and the 24576-key tile cuts the per-tile work (scans,
+// look-back, tile hand-out) per key; used once there is a tile for every CU.
+constexpr int kPairsBlock = 1024;
 constexpr int kPairsItems = 24;
-constexpr uint64_t kPairsLargeMinN = 256ull * kSortBlock * kPairsItems;
+constexpr uint64_t kPairsLargeMinN = 256ull * kPairsBlock * kPairsItems;
+// Large keys-only sorts: 32 keys per thread fit without values, and two
+// 512-thread blocks share a CU, so one block ranks while the other waits on
+// memory or on the look-back; used once every block (two per CU) has a tile.
+constexpr int kKeysBlock = 512;
+constexpr int kKeysItems = 32;
+constexpr uint64_t kKeysLargeMinN = 512ull * kKeysBlock * kKeysItems;
 // Up to this many keys the whole sort runs in one block, in LDS.
 constexpr uint32_t kTileSortMax = 16384;
 constexpr int kSortLookback = 2;       // earlier tiles read per look-back batch (a wave waits for
@@ -209,7 +216,8 @@ __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint
 // One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
 // tiles the scheduler hands it.
 template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
-__global__ __launch_bounds__(BLOCK) void onesweep_kernel(PassArgs a) {
+__global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
+void onesweep_kernel(PassArgs a) {
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
     constexpr int WAVE_KEYS = kWave * ITEMS;
@@ -583,11 +591,20 @@ struct SortLayout {
 constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
 constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
+enum class PassShape { kSmall, kPairsLarge, kKeysLarge };
+
+PassShape pass_shape(uint64_t n, bool pairs) {
+    if (pairs) return n >= kPairsLargeMinN ? PassShape::kPairsLarge : PassShape::kSmall;
+    return n >= kKeysLargeMinN ? PassShape::kKeysLarge : PassShape::kSmall;
+}
+
 // Keys per tile of the one-sweep pass.
 uint64_t pass_tile_keys(uint64_t n, bool pairs) {
-    if (pairs && n >= kPairsLargeMinN) return static_cast<uint64_t>(kSortBlock) * kPairsItems;
-    if (!pairs && n >= kKeysLargeMinN) return static_cast<uint64_t>(kSortBlock) * kKeysItems;
-    return static_cast<uint64_t>(kSortTile);
+    switch (pass_shape(n, pairs)) {
+    case PassShape::kPairsLarge: return static_cast<uint64_t>(kPairsBlock) * kPairsItems;
+    case PassShape::kKeysLarge: return static_cast<uint64_t>(kKeysBlock) * kKeysItems;
+    default: return static_cast<uint64_t>(kSortTile);
+    }
 }
 
 SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
@@ -637,19 +654,21 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int ITEMS, bool PAIRS>
+template <int BLOCK, int ITEMS, bool PAIRS>
 hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (flip_in && flip_out) return launch_pass_t<kSortBlock, ITEMS, PAIRS, true, true>(a, s);
-    if (flip_in) return launch_pass_t<kSortBlock, ITEMS, PAIRS, true, false>(a, s);
-    if (flip_out) return launch_pass_t<kSortBlock, ITEMS, PAIRS, false, true>(a, s);
-    return launch_pass_t<kSortBlock, ITEMS, PAIRS, false, false>(a, s);
+    if (flip_in && flip_out) return launch_pass_t<BLOCK, ITEMS, PAIRS, true, true>(a, s);
+    if (flip_in) return launch_pass_t<BLOCK, ITEMS, PAIRS, true, false>(a, s);
+    if (flip_out) return launch_pass_t<BLOCK, ITEMS, PAIRS, false, true>(a, s);
+    return launch_pass_t<BLOCK, ITEMS, PAIRS, false, false>(a, s);
 }
 
 template <bool PAIRS>
 hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (pass_tile_keys(a.n, PAIRS) != static_cast<uint64_t>(kSortTile))
-        return launch_pass_items<PAIRS ? kPairsItems : kKeysItems, PAIRS>(flip_in, flip_out, a, s);
-    return launch_pass_items<kSortItems, PAIRS>(flip_in, flip_out, a, s);
+    if (pass_shape(a.n, PAIRS) != PassShape::kSmall) {
+        if constexpr (PAIRS) return launch_pass_items<kPairsBlock, kPairsItems, true>(flip_in, flip_out, a, s);
+        else return launch_pass_items<kKeysBlock, kKeysItems, false>(flip_in, flip_out, a, s);
+    }
+    return launch_pass_items<kSortBlock, kSortItems, PAIRS>(flip_in, flip_out, a, s);
 }
 
 template <int BLOCK, int ITEMS, bool PAIRS>

@@ -21,11 +21,12 @@ pytestmark = pytest.mark.gpu
 # Sort paths: up to TILE keys one workgroup sorts in LDS (tile shapes of 1024,
 # 4096 and 16384 keys); above, the one-sweep passes use TILE-key tiles.  LARGE
 # is the first size at which every CU gets a tile; pair sorts switch to
-# PTILE-key tiles at PLARGE and keys-only sorts to 32768-key tiles at KLARGE.
+# PTILE-key tiles at PLARGE and keys-only sorts to 512-thread blocks of 32
+# keys each at KLARGE.
 TILE = 16384
 STILE = 4096
 LARGE = 256 * TILE
-KLARGE = 256 * 2 * TILE  # keys-only sorts use 32768-key tiles from here on
+KLARGE = 512 * TILE  # keys-only sorts switch to 512 x 32 tiles (two blocks per CU) here
 PTILE = 24576  # keys per tile of a pair sort from PLARGE on
 PLARGE = 256 * PTILE
 CTILE = 32768  # floats per tile of the compaction
