@@ -59,7 +59,7 @@ constexpr int kGroups = 8;             // XCDs
 // Cache-policy operand of a buffer access: the non-temporal bit.
 constexpr int kNonTemporal = 2;
 
-constexpr int kUpBlock = 256;
+constexpr int kUpBlock = 1024;   // many waves per CU hide the LDS atomics' latency
 constexpr int kUpSub = 8;          // sub-histograms per digit (spreads LDS atomics)
 constexpr int kMaxPasses = 4;
 
@@ -694,7 +694,7 @@ void launch_tile_sort(const uint32_t* ki, uint32_t* ko, const uint32_t* vi, uint
 
 int upsweep_grid(uint32_t n) {
     const int cus = device_cus();
-    const uint64_t vec_per_block = static_cast<uint64_t>(kUpBlock) * 16;   // >= 16 uint4 per thread
+    const uint64_t vec_per_block = static_cast<uint64_t>(kUpBlock) * 4;   // >= 4 uint4 per thread
     uint64_t g = (static_cast<uint64_t>(n) / 4 + vec_per_block - 1) / vec_per_block;
     if (g < 1) g = 1;
     if (g > static_cast<uint64_t>(cus) * 4) g = static_cast<uint64_t>(cus) * 4;
