@@ -51,9 +51,12 @@ constexpr int kKeysItems = 32;
 constexpr uint64_t kKeysLargeMinN = 512ull * kKeysBlock * kKeysItems;
 // Up to this many keys the whole sort runs in one block, in LDS.
 constexpr uint32_t kTileSortMax = 16384;
-constexpr int kSortLookback = 2;       // earlier tiles read per look-back batch (a wave waits for
-                                       // every state of a batch that any of its lanes still needs;
-                                       // 2 measured best, 8 is 2-4 % slower)
+// Earlier tiles read per look-back batch.  A wave waits for every word of a
+// batch that any of its lanes still needs, so small batches win: 2 measured
+// best for the 16384-key tiles (8 is 2-4 % slower), 1 for the 24576-key pair
+// tiles (1 % faster than 2 there, 1-2 % slower elsewhere).
+constexpr int kSortLookback = 2;
+constexpr int kPairsLookback = 1;
 constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
 constexpr int kGroups = 8;             // XCDs
 // Cache-policy operand of a buffer access: the non-temporal bit.
@@ -641,10 +644,10 @@ uint32_t resident_blocks(K kernel, int block) {
     return r < kMaxResidentBlocks ? r : kMaxResidentBlocks;
 }
 
-template <int BLOCK, int ITEMS, bool PAIRS, bool FI, bool FO>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO>
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     static uint32_t resident = 0;
-    auto kern = onesweep_kernel<BLOCK, ITEMS, kSortLookback, PAIRS, FI, FO>;
+    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO>;
     if (resident == 0) resident = resident_blocks(kern, BLOCK);
     const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
@@ -654,21 +657,23 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BLOCK, int ITEMS, bool PAIRS>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS>
 hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (flip_in && flip_out) return launch_pass_t<BLOCK, ITEMS, PAIRS, true, true>(a, s);
-    if (flip_in) return launch_pass_t<BLOCK, ITEMS, PAIRS, true, false>(a, s);
-    if (flip_out) return launch_pass_t<BLOCK, ITEMS, PAIRS, false, true>(a, s);
-    return launch_pass_t<BLOCK, ITEMS, PAIRS, false, false>(a, s);
+    if (flip_in && flip_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, true>(a, s);
+    if (flip_in) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, false>(a, s);
+    if (flip_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, true>(a, s);
+    return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false>(a, s);
 }
 
 template <bool PAIRS>
 hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
     if (pass_shape(a.n, PAIRS) != PassShape::kSmall) {
-        if constexpr (PAIRS) return launch_pass_items<kPairsBlock, kPairsItems, true>(flip_in, flip_out, a, s);
-        else return launch_pass_items<kKeysBlock, kKeysItems, false>(flip_in, flip_out, a, s);
+        if constexpr (PAIRS)
+            return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(flip_in, flip_out, a, s);
+        else
+            return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
     }
-    return launch_pass_items<kSortBlock, kSortItems, PAIRS>(flip_in, flip_out, a, s);
+    return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(flip_in, flip_out, a, s);
 }
 
 template <int BLOCK, int ITEMS, bool PAIRS>
