@@ -218,9 +218,16 @@ __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint
 
 // One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
 // tiles the scheduler hands it.
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
+//
+// ANY_ORDER: the keys of one row that share a digit may take their slots in
+// any order (LDS atomics instead of the ballot rank).  Only valid where such
+// keys are interchangeable in the final result: the first pass of a keys-only
+// sort over all 32 bits, since every later pass is stable and keys equal in
+// all their digits are equal keys.
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT, bool ANY_ORDER>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
 void onesweep_kernel(PassArgs a) {
+    static_assert(!(ANY_ORDER && PAIRS), "values need the stable rank");
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
     constexpr int WAVE_KEYS = kWave * ITEMS;
@@ -249,6 +256,10 @@ void onesweep_kernel(PassArgs a) {
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
+    // Same-address LDS atomics serialise, so the any-order rank is kept for
+    // passes where no digit holds more than half of the keys.
+    bool atomic_rank = false;
+    if constexpr (ANY_ORDER) atomic_rank = !__syncthreads_or(2ull * bin > n);
 
     for (;;) {
         // A tile is taken only when the block can start on it at once: the
@@ -281,19 +292,29 @@ void onesweep_kernel(PassArgs a) {
         // rank in the wave, later the position in the tile: 16 bits, two per register
         uint32_t pos[ITEMS / 2];
         uint32_t* my_count = s_off + wave * kRadix;
+        if (ANY_ORDER && atomic_rank) {   // uniform
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
-            const uint32_t before = my_count[d];
-            const uint64_t others = lanes_with_other_digit(d);
-            const uint32_t below = lane - count_below(others);      // same digit, lower lane
-            const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
-            if (below == 0) my_count[d] = before + group_size;
-            if (j % 2 == 0) pos[j / 2] = before + below;
-            else pos[j / 2] |= (before + below) << 16;
-            // the slots are chained through the LDS counters anyway; keeping the
-            // scheduler from interleaving them keeps register pressure low
-            __builtin_amdgcn_sched_barrier(0);
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+                const uint32_t slot = atomicAdd(&my_count[d], 1u);   // distinct per key
+                if (j % 2 == 0) pos[j / 2] = slot;
+                else pos[j / 2] |= slot << 16;
+            }
+        } else {
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+                const uint32_t before = my_count[d];
+                const uint64_t others = lanes_with_other_digit(d);
+                const uint32_t below = lane - count_below(others);      // same digit, lower lane
+                const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
+                if (below == 0) my_count[d] = before + group_size;
+                if (j % 2 == 0) pos[j / 2] = before + below;
+                else pos[j / 2] |= (before + below) << 16;
+                // the slots are chained through the LDS counters anyway; keeping the
+                // scheduler from interleaving them keeps register pressure low
+                __builtin_amdgcn_sched_barrier(0);
+            }
         }
         __syncthreads();
 
@@ -644,10 +665,10 @@ uint32_t resident_blocks(K kernel, int block) {
     return r < kMaxResidentBlocks ? r : kMaxResidentBlocks;
 }
 
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO, bool ANY_ORDER = false>
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     static uint32_t resident = 0;
-    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO>;
+    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO, ANY_ORDER>;
     if (resident == 0) resident = resident_blocks(kern, BLOCK);
     const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
@@ -665,13 +686,17 @@ hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hip
     return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false>(a, s);
 }
 
+// any_order: see onesweep_kernel (used by large keys-only sorts only).
 template <bool PAIRS>
-hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
+hipError_t launch_pass(bool flip_in, bool flip_out, bool any_order, const PassArgs& a, hipStream_t s) {
     if (pass_shape(a.n, PAIRS) != PassShape::kSmall) {
-        if constexpr (PAIRS)
+        if constexpr (PAIRS) {
             return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(flip_in, flip_out, a, s);
-        else
+        } else {
+            if (any_order && !flip_in && !flip_out)
+                return launch_pass_t<kKeysBlock, kKeysItems, kSortLookback, false, false, false, true>(a, s);
             return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
+        }
     }
     return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(flip_in, flip_out, a, s);
 }
@@ -815,8 +840,10 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
         const bool flip_in = is_f32 && p == 0;
         const bool flip_out = is_f32 && p == passes - 1;
         timing_before(stream, RS_KERNEL_ONESWEEP);
-        e = pairs ? launch_pass<true>(flip_in, flip_out, a, stream)
-                  : launch_pass<false>(flip_in, flip_out, a, stream);
+        // Equal keys are interchangeable only in a keys-only sort over the whole key.
+        const bool any_order = !pairs && !is_f32 && p == 0 && begin_bit == 0 && end_bit == 32;
+        e = pairs ? launch_pass<true>(flip_in, flip_out, false, a, stream)
+                  : launch_pass<false>(flip_in, flip_out, any_order, a, stream);
         timing_after(stream);
         if (e != hipSuccess) return e;
         sk = a.dst_keys;

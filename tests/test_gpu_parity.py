@@ -62,30 +62,47 @@ def test_pairs_u32_bit_ranges(n, b, e):
     check_pairs(rng(n + b * 33 + e).integers(0, 2**32, n, dtype=np.uint32), b, e)
 
 
-@pytest.mark.parametrize("kind", ["all_equal", "all_max", "single_digit", "few_values",
-                                  "sorted", "reversed", "zipf", "top_byte_only"])
-@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE + 1234, PLARGE + 1234])
-def test_pairs_u32_distributions(kind, n):
+DISTRIBUTIONS = ["all_equal", "all_max", "single_digit", "few_values", "sorted", "reversed", "zipf",
+                 "top_byte_only"]
+
+
+def dist_keys(kind, n):
     r = rng(11)
     if kind == "all_equal":
-        keys = np.full(n, 0x12345678, np.uint32)
-    elif kind == "all_max":
-        keys = np.full(n, 0xFFFFFFFF, np.uint32)
-    elif kind == "single_digit":
-        keys = (r.integers(0, 2**32, n, dtype=np.uint32) & np.uint32(0xFFFF00FF)) | np.uint32(0x5A00)
-    elif kind == "few_values":
-        keys = r.integers(0, 5, n, dtype=np.uint32) * np.uint32(0x01000001)
-    elif kind == "sorted":
-        keys = np.sort(r.integers(0, 2**32, n, dtype=np.uint32))
-    elif kind == "reversed":
-        keys = np.sort(r.integers(0, 2**32, n, dtype=np.uint32))[::-1].copy()
-    elif kind == "zipf":
-        keys = workloads.zipf_u32(n, seed=3)
-    else:
-        keys = r.integers(0, 256, n, dtype=np.uint32) << np.uint32(24)
+        return np.full(n, 0x12345678, np.uint32)
+    if kind == "all_max":
+        return np.full(n, 0xFFFFFFFF, np.uint32)
+    if kind == "single_digit":
+        return (r.integers(0, 2**32, n, dtype=np.uint32) & np.uint32(0xFFFF00FF)) | np.uint32(0x5A00)
+    if kind == "few_values":
+        return r.integers(0, 5, n, dtype=np.uint32) * np.uint32(0x01000001)
+    if kind == "sorted":
+        return np.sort(r.integers(0, 2**32, n, dtype=np.uint32))
+    if kind == "reversed":
+        return np.sort(r.integers(0, 2**32, n, dtype=np.uint32))[::-1].copy()
+    if kind == "zipf":
+        return workloads.zipf_u32(n, seed=3)
+    return r.integers(0, 256, n, dtype=np.uint32) << np.uint32(24)
+
+
+@pytest.mark.parametrize("kind", DISTRIBUTIONS)
+@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE + 1234, PLARGE + 1234])
+def test_pairs_u32_distributions(kind, n):
+    keys = dist_keys(kind, n)
     print("pairs u32 distribution=%s n=%d" % (kind, n), flush=True)
     for (b, e) in [(0, 32), (0, 16), (16, 32)]:
         check_pairs(keys, b, e)
+
+
+@pytest.mark.parametrize("kind", DISTRIBUTIONS)
+@pytest.mark.parametrize("n", [3 * TILE + 1234, KLARGE + 1234])
+def test_keys_u32_distributions(kind, n):
+    """Skewed inputs through both keys-only pass shapes (the first full-range pass of the
+    large shape ranks equal keys of a row in any order)."""
+    keys = dist_keys(kind, n)
+    print("keys u32 distribution=%s n=%d" % (kind, n), flush=True)
+    for (b, e) in [(0, 32), (0, 16), (16, 32)]:
+        assert np.array_equal(gpu_sort_keys_u32(keys, b, e), oracle.sort_u32(keys, None, b, e)), (b, e)
 
 
 @pytest.mark.parametrize("n", [1, 64, 1000, 4000, TILE, TILE + 1, 3 * TILE + 17, (1 << 20) + 17,
