@@ -233,6 +233,7 @@ void onesweep_kernel(PassArgs a) {
     constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
     static_assert(TILE <= 32768, "16-bit positions");
+    static_assert(TILE * 4 >= WAVES * kRadix * 8, "lane masks fit the staging buffer");
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
 
     // One staging buffer: the keys in digit order, then the values in digit order.
@@ -256,10 +257,13 @@ void onesweep_kernel(PassArgs a) {
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
-    // Same-address LDS atomics serialise, so the any-order rank is kept for
-    // passes where no digit holds more than half of the keys.
-    bool atomic_rank = false;
+    // Same-address LDS atomics serialise, so the LDS ranks below are kept for
+    // passes whose digits are spread out: the any-order rank while no digit
+    // holds more than half of the keys, the lane-mask rank while none holds
+    // more than an eighth.
+    bool atomic_rank = false, mask_rank = false;
     if constexpr (ANY_ORDER) atomic_rank = !__syncthreads_or(2ull * bin > n);
+    if constexpr (PAIRS) mask_rank = !__syncthreads_or(8ull * bin > n);
 
     for (;;) {
         // A tile is taken only when the block can start on it at once: the
@@ -272,6 +276,13 @@ void onesweep_kernel(PassArgs a) {
         __syncthreads();
         const uint32_t tile = s_next;
         if (tile >= tiles) break;   // uniform: no tiles left
+        // Half of the waves (two per SIMD) rank with LDS lane masks and half
+        // with ballots, so that the LDS and the VALU share the rank's work.
+        // The masks live in the staging buffer, unused until the re-layout.
+        const bool lds_rank = mask_rank && (wave & 4u) != 0u;   // uniform per wave
+        unsigned long long* my_masks = reinterpret_cast<unsigned long long*>(s_buf) + wave * kRadix;
+        if (lds_rank)
+            for (uint32_t i = lane; i < kRadix; i += kWave) my_masks[i] = 0ull;
         uint32_t k[ITEMS];
         load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
         const uint32_t tile_base = tile * TILE;
@@ -299,6 +310,28 @@ void onesweep_kernel(PassArgs a) {
                 const uint32_t slot = atomicAdd(&my_count[d], 1u);   // distinct per key
                 if (j % 2 == 0) pos[j / 2] = slot;
                 else pos[j / 2] |= slot << 16;
+            }
+        } else if (lds_rank) {
+            // Lane-mask rank: every lane ORs its bit into its digit's mask; the
+            // mask read back is the set of lanes with that digit (one wave's LDS
+            // instructions execute in order).  The lowest such lane advances the
+            // counter and clears the mask for the next row.
+            const unsigned long long lane_bit = 1ull << lane;
+#pragma unroll
+            for (int j = 0; j < ITEMS; ++j) {
+                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+                atomicOr(&my_masks[d], lane_bit);
+                const unsigned long long same =
+                    __hip_atomic_load(&my_masks[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
+                const uint32_t before = my_count[d];
+                const uint32_t below = count_below(same);   // same digit, lower lane
+                if (below == 0) {
+                    my_count[d] = before + static_cast<uint32_t>(__popcll(same));
+                    my_masks[d] = 0ull;
+                }
+                if (j % 2 == 0) pos[j / 2] = before + below;
+                else pos[j / 2] |= (before + below) << 16;
+                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
