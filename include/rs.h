@@ -28,8 +28,11 @@
  *    nothing is launched; otherwise *temp_bytes must be at least that size.
  *    The caller owns the temp buffer and need not initialise it.  The size
  *    depends only on n (and on whether values are sorted).
- *  - The library keeps no mutable state between calls: concurrent calls on
- *    different streams with different temp buffers are independent.
+ *  - The library keeps no mutable state between calls (apart from the
+ *    opt-in timing hook below): concurrent calls on different streams with
+ *    different temp buffers are independent.  Launch grids are sized once
+ *    per process from the device current at the first call; a grid only
+ *    affects speed, never results.
  *  - n < 2^30 (RS_ERR_UNSUPPORTED_SIZE otherwise): cross-tile prefix states
  *    hold 30-bit counts beside 2 status bits.
  */

@@ -196,15 +196,14 @@ CompactLayout compact_layout(uint64_t n) {
 }
 
 uint32_t compact_resident() {
-    static uint32_t resident = 0;
-    if (resident == 0) {
+    static const uint32_t resident = [] {   // thread-safe one-time init
         int per_cu = 0;
         if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, compact_kernel, kCompBlock, 0) !=
                 hipSuccess ||
             per_cu <= 0)
             per_cu = 1;
-        resident = static_cast<uint32_t>(per_cu) * static_cast<uint32_t>(device_cus());
-    }
+        return static_cast<uint32_t>(per_cu) * static_cast<uint32_t>(device_cus());
+    }();
     return resident;
 }
 

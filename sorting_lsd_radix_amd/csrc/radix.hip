@@ -700,9 +700,8 @@ uint32_t resident_blocks(K kernel, int block) {
 
 template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO, bool ANY_ORDER = false>
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
-    static uint32_t resident = 0;
     auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO, ANY_ORDER>;
-    if (resident == 0) resident = resident_blocks(kern, BLOCK);
+    static const uint32_t resident = resident_blocks(kern, BLOCK);   // one-time init
     const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
     b.groups = g.groups;
@@ -778,15 +777,18 @@ TileGrid tile_grid(uint32_t tiles, uint32_t resident) {
     return g;
 }
 
+// CUs of the device current at the first call (thread-safe one-time init).
+// Grids only size the persistent launches: any count is correct, since
+// blocks take their tiles dynamically.
 int device_cus() {
-    static int cus = 0;
-    if (cus == 0) {
-        int dev = 0;
+    static const int cus = [] {
+        int dev = 0, c = 0;
         if (hipGetDevice(&dev) != hipSuccess ||
-            hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-            cus <= 0)
-            cus = 256;
-    }
+            hipDeviceGetAttribute(&c, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+            c <= 0)
+            c = 256;
+        return c;
+    }();
     return cus;
 }
 
