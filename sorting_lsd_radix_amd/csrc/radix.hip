@@ -220,13 +220,7 @@ __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint
 // One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
 // tiles the scheduler hands it.
 //
-// ATOMIC_RANK: rank with one LDS atomic add per key.  On gfx950 the lanes of
-// one ds_add_rtn_u32 that hit the same address are served in lane order, so
-// the values returned are exactly the stable in-wave rank (before + lanes
-// below with the same digit); a GPU test checks this property directly, and
-// the parity tests check every sort that relies on it.  Used by the large
-// keys-only shape, where it is 9 % faster than the ballot rank.
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT, bool ATOMIC_RANK>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
 void onesweep_kernel(PassArgs a) {
     constexpr int WAVES = BLOCK / kWave;
@@ -234,7 +228,6 @@ void onesweep_kernel(PassArgs a) {
     constexpr int WAVE_KEYS = kWave * ITEMS;
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
     static_assert(TILE <= 32768, "16-bit positions");
-    static_assert(TILE * 4 >= WAVES * kRadix * 8, "lane masks fit the staging buffer");
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
 
     // One staging buffer: the keys in digit order, then the values in digit order.
@@ -259,18 +252,15 @@ void onesweep_kernel(PassArgs a) {
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
-    // Same-address LDS atomics serialise, so the LDS ranks below are kept for
-    // passes whose digits are spread out: the atomic rank while no digit holds
-    // more than a fraction 2^-atomic_limit_log2 of the keys, and in each block
-    // until a tile has a digit over that fraction of its keys (earlier passes
-    // gather equal keys into runs, which then collide within a row); the
-    // lane-mask rank while no digit holds more than 1/8 of the keys.
-    bool mask_rank = false;
-    if constexpr (ATOMIC_RANK) {
+    // Same-address LDS atomics serialise, so the atomic rank below is kept
+    // while no digit holds more than a share 2^-atomic_limit_log2 of the
+    // pass's keys, and in each block until one of its tiles has a digit over
+    // that share of the tile (earlier passes gather equal keys into runs,
+    // which then collide within a row); otherwise the ballot rank.
+    {
         const bool spread = !__syncthreads_or((static_cast<uint64_t>(bin) << a.atomic_limit_log2) > n);
         if (tid == 0) s_atomic_rank = spread ? 1u : 0u;   // read after the loop's first barrier
     }
-    if constexpr (PAIRS) mask_rank = !__syncthreads_or(8ull * bin > n);
 
     for (;;) {
         // A tile is taken only when the block can start on it at once: the
@@ -283,13 +273,6 @@ void onesweep_kernel(PassArgs a) {
         __syncthreads();
         const uint32_t tile = s_next;
         if (tile >= tiles) break;   // uniform: no tiles left
-        // Half of the waves (two per SIMD) rank with LDS lane masks and half
-        // with ballots, so that the LDS and the VALU share the rank's work.
-        // The masks live in the staging buffer, unused until the re-layout.
-        const bool lds_rank = mask_rank && (wave & 4u) != 0u;   // uniform per wave
-        unsigned long long* my_masks = reinterpret_cast<unsigned long long*>(s_buf) + wave * kRadix;
-        if (lds_rank)
-            for (uint32_t i = lane; i < kRadix; i += kWave) my_masks[i] = 0ull;
         uint32_t k[ITEMS];
         load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
         const uint32_t tile_base = tile * TILE;
@@ -310,35 +293,19 @@ void onesweep_kernel(PassArgs a) {
         // rank in the wave, later the position in the tile: 16 bits, two per register
         uint32_t pos[ITEMS / 2];
         uint32_t* my_count = s_off + wave * kRadix;
-        if (ATOMIC_RANK && s_atomic_rank != 0u) {   // uniform
+        if (s_atomic_rank != 0u) {   // uniform
+            // Atomic rank: one LDS atomic add per key on the wave's digit
+            // counter.  On gfx950 the lanes of one ds_add_rtn_u32 that hit the
+            // same address are served in lane order, so each lane gets the
+            // counter plus the lanes below it with the same digit: the stable
+            // rank.  This is observed behaviour, which a GPU test of the
+            // hardware checks directly and every parity test depends on.
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
                 const uint32_t slot = atomicAdd(&my_count[d], 1u);   // served in lane order
                 if (j % 2 == 0) pos[j / 2] = slot;
                 else pos[j / 2] |= slot << 16;
-            }
-        } else if (lds_rank) {
-            // Lane-mask rank: every lane ORs its bit into its digit's mask; the
-            // mask read back is the set of lanes with that digit (one wave's LDS
-            // instructions execute in order).  The lowest such lane advances the
-            // counter and clears the mask for the next row.
-            const unsigned long long lane_bit = 1ull << lane;
-#pragma unroll
-            for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
-                atomicOr(&my_masks[d], lane_bit);
-                const unsigned long long same =
-                    __hip_atomic_load(&my_masks[d], __ATOMIC_RELAXED, __HIP_MEMORY_SCOPE_WORKGROUP);
-                const uint32_t before = my_count[d];
-                const uint32_t below = count_below(same);   // same digit, lower lane
-                if (below == 0) {
-                    my_count[d] = before + static_cast<uint32_t>(__popcll(same));
-                    my_masks[d] = 0ull;
-                }
-                if (j % 2 == 0) pos[j / 2] = before + below;
-                else pos[j / 2] |= (before + below) << 16;
-                __builtin_amdgcn_sched_barrier(0);
             }
         } else {
 #pragma unroll
@@ -368,7 +335,7 @@ void onesweep_kernel(PassArgs a) {
                 count += c;
             }
         }
-        if (ATOMIC_RANK && (count << a.atomic_limit_log2) > static_cast<uint32_t>(TILE))
+        if ((count << a.atomic_limit_log2) > static_cast<uint32_t>(TILE))
             s_atomic_rank = 0u;   // from the next tile on
         // the padding of a partial tile sits in the last digit; it is not published
         const uint32_t pads = static_cast<uint32_t>(TILE) - valid;
@@ -707,9 +674,9 @@ uint32_t resident_blocks(K kernel, int block) {
     return r < kMaxResidentBlocks ? r : kMaxResidentBlocks;
 }
 
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO, bool ATOMIC_RANK = false>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO>
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
-    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO, ATOMIC_RANK>;
+    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO>;
     static const uint32_t resident = resident_blocks(kern, BLOCK);   // one-time init
     const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
@@ -732,8 +699,6 @@ hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream
     if (pass_shape(a.n, PAIRS) != PassShape::kSmall) {
         if constexpr (PAIRS)
             return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(flip_in, flip_out, a, s);
-        else if (!flip_in && !flip_out)   // the library's keys-only sorts never flip
-            return launch_pass_t<kKeysBlock, kKeysItems, kSortLookback, false, false, false, true>(a, s);
         else
             return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
     }
