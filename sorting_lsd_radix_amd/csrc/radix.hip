@@ -218,8 +218,9 @@ __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint
 }
 
 // One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
-// tiles the scheduler hands it.
-//
+// tiles the scheduler hands it.  Per tile: load, stable in-wave rank (LDS
+// atomics or ballots), tile counts and scans, decoupled look-back, re-layout
+// in digit order in LDS, scatter of each digit run.
 template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
 void onesweep_kernel(PassArgs a) {
