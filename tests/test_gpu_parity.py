@@ -63,7 +63,7 @@ def test_pairs_u32_bit_ranges(n, b, e):
 
 
 DISTRIBUTIONS = ["all_equal", "all_max", "single_digit", "few_values", "sorted", "reversed", "zipf",
-                 "top_byte_only"]
+                 "top_byte_only", "card24", "card300"]
 
 
 def dist_keys(kind, n):
@@ -82,6 +82,11 @@ def dist_keys(kind, n):
         return np.sort(r.integers(0, 2**32, n, dtype=np.uint32))[::-1].copy()
     if kind == "zipf":
         return workloads.zipf_u32(n, seed=3)
+    if kind in ("card24", "card300"):
+        # few distinct full-width keys: after the first pass equal keys form runs in every tile,
+        # so tiles switch between the atomic and the ballot rank
+        distinct = r.integers(0, 2**32, 24 if kind == "card24" else 300, dtype=np.uint32)
+        return distinct[r.integers(0, distinct.size, n)]
     return r.integers(0, 256, n, dtype=np.uint32) << np.uint32(24)
 
 
