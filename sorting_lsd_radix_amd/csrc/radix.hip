@@ -37,12 +37,15 @@ constexpr int kPassWavesPerSimd = 4;
 constexpr int kSortBlock = 1024;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
-// Large pair sorts: 24 keys and values per thread still fit the registers
-// (28 spills), and the 24576-key tile cuts the per-tile work (scans,
-// look-back, tile hand-out) per key; used once there is a tile for every CU.
+// Large pair sorts: bigger tiles cut the per-tile work (scans, look-back,
+// tile hand-out) per key.  24 keys and values per thread from the size that
+// gives every CU a tile; 28 (32 spills) once there are at least 2^26 keys,
+// below which the last round of tiles leaves too many CUs idle.
 constexpr int kPairsBlock = 1024;
 constexpr int kPairsItems = 24;
 constexpr uint64_t kPairsLargeMinN = 256ull * kPairsBlock * kPairsItems;
+constexpr int kPairsHugeItems = 28;
+constexpr uint64_t kPairsHugeMinN = 1ull << 26;
 // Large keys-only sorts: 32 keys per thread fit without values, and two
 // 512-thread blocks share a CU, so one block ranks while the other waits on
 // memory or on the look-back; used once every block (two per CU) has a tile.
@@ -626,10 +629,13 @@ struct SortLayout {
 constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
 constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
-enum class PassShape { kSmall, kPairsLarge, kKeysLarge };
+enum class PassShape { kSmall, kPairsLarge, kPairsHuge, kKeysLarge };
 
 PassShape pass_shape(uint64_t n, bool pairs) {
-    if (pairs) return n >= kPairsLargeMinN ? PassShape::kPairsLarge : PassShape::kSmall;
+    if (pairs) {
+        if (n >= kPairsHugeMinN) return PassShape::kPairsHuge;
+        return n >= kPairsLargeMinN ? PassShape::kPairsLarge : PassShape::kSmall;
+    }
     return n >= kKeysLargeMinN ? PassShape::kKeysLarge : PassShape::kSmall;
 }
 
@@ -637,6 +643,7 @@ PassShape pass_shape(uint64_t n, bool pairs) {
 uint64_t pass_tile_keys(uint64_t n, bool pairs) {
     switch (pass_shape(n, pairs)) {
     case PassShape::kPairsLarge: return static_cast<uint64_t>(kPairsBlock) * kPairsItems;
+    case PassShape::kPairsHuge: return static_cast<uint64_t>(kPairsBlock) * kPairsHugeItems;
     case PassShape::kKeysLarge: return static_cast<uint64_t>(kKeysBlock) * kKeysItems;
     default: return static_cast<uint64_t>(kSortTile);
     }
@@ -698,10 +705,14 @@ hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hip
 
 template <bool PAIRS>
 hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (pass_shape(a.n, PAIRS) != PassShape::kSmall) {
-        if constexpr (PAIRS)
+    const PassShape shape = pass_shape(a.n, PAIRS);
+    if (shape != PassShape::kSmall) {
+        if constexpr (PAIRS) {
+            if (shape == PassShape::kPairsHuge)
+                return launch_pass_items<kPairsBlock, kPairsHugeItems, kPairsLookback, true>(flip_in, flip_out, a,
+                                                                                             s);
             return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(flip_in, flip_out, a, s);
-        else
+        } else
             return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
     }
     return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(flip_in, flip_out, a, s);

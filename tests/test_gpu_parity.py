@@ -29,6 +29,8 @@ LARGE = 256 * TILE
 KLARGE = 512 * TILE  # keys-only sorts switch to 512 x 32 tiles (two blocks per CU) here
 PTILE = 24576  # keys per tile of a pair sort from PLARGE on
 PLARGE = 256 * PTILE
+HTILE = 28672  # keys per tile of a pair sort from HLARGE on
+HLARGE = 1 << 26
 CTILE = 32768  # floats per tile of the compaction
 SIZES = [1, 2, 63, 64, 65, 1000, 1024, 1025, STILE, STILE + 1, TILE - 1, TILE, TILE + 1,
          3 * TILE + 17, (1 << 20) + 17, LARGE - 1, LARGE, LARGE + 17, PLARGE - 1, PLARGE,
@@ -97,6 +99,15 @@ def test_pairs_u32_distributions(kind, n):
     print("pairs u32 distribution=%s n=%d" % (kind, n), flush=True)
     for (b, e) in [(0, 32), (0, 16), (16, 32)]:
         check_pairs(keys, b, e)
+
+
+@pytest.mark.parametrize("n", [HLARGE - 1, HLARGE + 3 * HTILE + 17])
+def test_pairs_u32_huge_tiles(n):
+    """Either side of the switch to 28672-key pair tiles, with a partial last tile."""
+    print("pairs u32 huge tiles n=%d" % n, flush=True)
+    keys = rng(n).integers(0, 2**32, n, dtype=np.uint32)
+    keys[: n // 4] &= np.uint32(0xFFFF00FF)   # a quarter with a common middle byte: clustered tiles
+    check_pairs(keys, 0, 32)
 
 
 @pytest.mark.parametrize("kind", DISTRIBUTIONS)
