@@ -52,6 +52,10 @@ constexpr uint64_t kPairsHugeMinN = 1ull << 26;
 constexpr int kKeysBlock = 512;
 constexpr int kKeysItems = 32;
 constexpr uint64_t kKeysLargeMinN = 512ull * kKeysBlock * kKeysItems;
+// From 2^27 keys (16 tiles per CU) one 1024 x 32 block per CU is faster:
+// half as many tiles in flight shorten every look-back walk.
+constexpr int kKeysHugeBlock = 1024;
+constexpr uint64_t kKeysHugeMinN = 1ull << 27;
 // Up to this many keys the whole sort runs in one block, in LDS.
 constexpr uint32_t kTileSortMax = 16384;
 // Earlier tiles read per look-back batch.  A wave waits for every word of a
@@ -629,13 +633,14 @@ struct SortLayout {
 constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
 constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
-enum class PassShape { kSmall, kPairsLarge, kPairsHuge, kKeysLarge };
+enum class PassShape { kSmall, kPairsLarge, kPairsHuge, kKeysLarge, kKeysHuge };
 
 PassShape pass_shape(uint64_t n, bool pairs) {
     if (pairs) {
         if (n >= kPairsHugeMinN) return PassShape::kPairsHuge;
         return n >= kPairsLargeMinN ? PassShape::kPairsLarge : PassShape::kSmall;
     }
+    if (n >= kKeysHugeMinN) return PassShape::kKeysHuge;
     return n >= kKeysLargeMinN ? PassShape::kKeysLarge : PassShape::kSmall;
 }
 
@@ -645,6 +650,7 @@ uint64_t pass_tile_keys(uint64_t n, bool pairs) {
     case PassShape::kPairsLarge: return static_cast<uint64_t>(kPairsBlock) * kPairsItems;
     case PassShape::kPairsHuge: return static_cast<uint64_t>(kPairsBlock) * kPairsHugeItems;
     case PassShape::kKeysLarge: return static_cast<uint64_t>(kKeysBlock) * kKeysItems;
+    case PassShape::kKeysHuge: return static_cast<uint64_t>(kKeysHugeBlock) * kKeysItems;
     default: return static_cast<uint64_t>(kSortTile);
     }
 }
@@ -712,8 +718,11 @@ hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream
                 return launch_pass_items<kPairsBlock, kPairsHugeItems, kPairsLookback, true>(flip_in, flip_out, a,
                                                                                              s);
             return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(flip_in, flip_out, a, s);
-        } else
+        } else {
+            if (shape == PassShape::kKeysHuge)
+                return launch_pass_items<kKeysHugeBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
             return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
+        }
     }
     return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(flip_in, flip_out, a, s);
 }

@@ -101,6 +101,16 @@ def test_pairs_u32_distributions(kind, n):
         check_pairs(keys, b, e)
 
 
+@pytest.mark.parametrize("b,e", [(0, 32), (3, 29)])
+def test_keys_u32_huge_tiles(b, e):
+    """Keys-only sorts from 2^27 keys use one 1024 x 32 block per CU (32768-key tiles)."""
+    n = (1 << 27) + 3 * 32768 + 17
+    print("keys u32 huge tiles n=%d bits=[%d,%d)" % (n, b, e), flush=True)
+    keys = rng(n + b).integers(0, 2**32, n, dtype=np.uint32)
+    keys[: n // 4] &= np.uint32(0xFF00FFFF)
+    assert np.array_equal(gpu_sort_keys_u32(keys, b, e), oracle.sort_u32(keys, None, b, e))
+
+
 @pytest.mark.parametrize("n", [HLARGE - 1, HLARGE + 3 * HTILE + 17])
 def test_pairs_u32_huge_tiles(n):
     """Either side of the switch to 28672-key pair tiles, with a partial last tile."""
