@@ -549,19 +549,18 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
         // this wave's counters; their readers in the previous pass all passed a barrier since
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
 
+        // Stable rank with one LDS atomic add per key (same-address lanes of
+        // one instruction are served in lane order on gfx950, as in the
+        // one-sweep pass; at these sizes the serialisation of crowded digits
+        // costs little, so no ballot fallback).
         uint32_t pos[ITEMS / 2];
         uint32_t* my_count = s_off + wave * kRadix;
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
-            const uint32_t before = my_count[d];
-            const uint64_t others = lanes_with_other_digit(d);
-            const uint32_t below = lane - count_below(others);
-            const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
-            if (below == 0) my_count[d] = before + group_size;
-            if (j % 2 == 0) pos[j / 2] = before + below;
-            else pos[j / 2] |= (before + below) << 16;
-            __builtin_amdgcn_sched_barrier(0);
+            const uint32_t slot = atomicAdd(&my_count[d], 1u);   // served in lane order
+            if (j % 2 == 0) pos[j / 2] = slot;
+            else pos[j / 2] |= slot << 16;
         }
         __syncthreads();
 
