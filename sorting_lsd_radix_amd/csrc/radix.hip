@@ -70,7 +70,11 @@ constexpr int kGroups = 8;             // XCDs
 constexpr int kNonTemporal = 2;
 
 constexpr int kUpBlock = 1024;   // many waves per CU hide the LDS atomics' latency
-constexpr int kUpSub = 8;          // sub-histograms per digit (spreads LDS atomics)
+// Sub-histograms per digit, indexed by lane mod 32 and stored innermost, so
+// the 32 lanes an LDS access serves together hit 32 different banks whatever
+// their digits (128 KB for four passes: one block per CU).  8 sub-histograms
+// (bank = lane mod 8 and two digit bits) took 14 % longer at 2^28 keys.
+constexpr int kUpSub = 32;
 constexpr int kMaxPasses = 4;
 
 constexpr size_t kAlign = 256;
@@ -157,10 +161,12 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
         count_key<FLIP>(s_hist, keys[nvec * 4 + threadIdx.x], pd, sub);
     __syncthreads();
 
+    // Thread i sums bin i's sub-histograms starting at sub i mod 32, so the
+    // lanes of one read hit different banks.
     for (uint32_t i = threadIdx.x; i < pd.passes * kRadix; i += kUpBlock) {
         uint32_t c = 0;
 #pragma unroll
-        for (int s = 0; s < kUpSub; ++s) c += s_hist[i * kUpSub + s];
+        for (int s = 0; s < kUpSub; ++s) c += s_hist[i * kUpSub + ((i + s) % kUpSub)];
         if (c) fetch_add_agent(&bins[i], c);
     }
 }
@@ -752,7 +758,7 @@ int upsweep_grid(uint32_t n) {
     const uint64_t vec_per_block = static_cast<uint64_t>(kUpBlock) * 4;   // >= 4 uint4 per thread
     uint64_t g = (static_cast<uint64_t>(n) / 4 + vec_per_block - 1) / vec_per_block;
     if (g < 1) g = 1;
-    if (g > static_cast<uint64_t>(cus) * 4) g = static_cast<uint64_t>(cus) * 4;
+    if (g > static_cast<uint64_t>(cus)) g = static_cast<uint64_t>(cus);   // one 128 KB block per CU
     return static_cast<int>(g);
 }
 
