@@ -13,8 +13,10 @@ The roofline entry is for the dominant kernel of the workload (the one-sweep
 pass for sorts, the one-workgroup tile sort for sorts of at most 16384 keys,
 the compaction kernel for compaction): its algorithmic bytes per launch over
 its mean duration, timed with HIP events that the library
-records around each of its launches on the call's stream during the timed
-steps.  Algorithmic bytes: 16 B per key per pass for key-value sorts (read and
+records around each of its launches on the call's stream during the last
+twentieth (at least one) of the timed steps, inside the same timed region
+(recording them in every step would add about 2 us per launch to the time per
+step).  Algorithmic bytes: 16 B per key per pass for key-value sorts (read and
 write key and value), 8 B for keys-only sorts, 8 B per element for compaction
 (read the input, write the output including the zero tail).  The CPU baseline
 is the oracle (single-threaded C) on a bounded prefix of the same workload.
@@ -162,12 +164,18 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         step()
     torch.cuda.synchronize()
 
-    rs.rs_timing_enable(True)
+    # One timed region of `steps` calls.  The library's per-launch events are
+    # recorded only during its last `event_steps` calls: each event still
+    # adds about 2 us between launches, which would otherwise inflate the
+    # time per step of small sorts by up to a third.
+    event_steps = max(1, steps // 20)
     start = torch.cuda.Event(enable_timing=True)
     stop = torch.cuda.Event(enable_timing=True)
     torch.cuda.synchronize()
     start.record(stream)
-    for _ in range(steps):
+    for i in range(steps):
+        if i == steps - event_steps:
+            rs.rs_timing_enable(True)
         step()
     stop.record(stream)
     torch.cuda.synchronize()
@@ -269,7 +277,8 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": dom, "algorithmic_bytes_per_launch": algo_bytes,
-                     "mean_launch_ms": round(dom_ms, 5)},
+                     "mean_launch_ms": round(dom_ms, 5), "timed_launches": len(per_kernel.get(dom, [])),
+                     "event_steps": event_steps},
         "whole_step_roofline_frac": round(algo_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()},
     }

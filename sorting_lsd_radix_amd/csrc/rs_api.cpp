@@ -105,8 +105,11 @@ void timing_before(hipStream_t s, int kernel_id) {
     std::lock_guard<std::mutex> lock(g_timing_mutex);
     if (!g_timing_enabled) return;
     TimingRecord r{kernel_id, nullptr, nullptr};
-    if (hipEventCreate(&r.start) != hipSuccess) return;
-    if (hipEventCreate(&r.stop) != hipSuccess) {
+    // Timing-only events: no system-scope fence (cache writeback and
+    // invalidation) when they are recorded, which would also slow the launch
+    // that follows.
+    if (hipEventCreateWithFlags(&r.start, hipEventDisableSystemFence) != hipSuccess) return;
+    if (hipEventCreateWithFlags(&r.stop, hipEventDisableSystemFence) != hipSuccess) {
         (void)hipEventDestroy(r.start);
         return;
     }
