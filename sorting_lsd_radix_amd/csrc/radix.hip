@@ -13,10 +13,15 @@
 //  * tile = BLOCK x ITEMS keys; a wave owns a contiguous run of 64 x ITEMS
 //    keys, loaded as ITEMS coalesced 256-byte rows (lane l of row j holds
 //    position j*64 + l), so rank order is (wave, row, lane) = input order;
-//  * the in-wave stable rank uses eight ballots to find the lanes holding
-//    the same digit, mbcnt to count the ones below, and a per-wave LDS
-//    counter per digit updated by one lane per digit group (no LDS atomics,
-//    one LDS write per distinct digit, so skewed inputs cost less, not more);
+//  * the stable rank inside a wave is one LDS atomic add per key on the
+//    wave's counter of its digit, whose same-address lanes the hardware
+//    serves in lane order (checked by a GPU test); while a digit is crowded
+//    it is instead eight ballots that find the lanes holding the same digit,
+//    mbcnt to count the ones below and one counter update per digit group
+//    (one LDS write per distinct digit, so skewed inputs cost less);
+//  * one upsweep block per CU counts every pass's digits into LDS
+//    sub-histograms laid out so that the lanes of an access hit distinct
+//    banks;
 //  * the tile is re-laid out in LDS in digit order so that each digit's run
 //    is written to HBM with consecutive addresses;
 //  * tile ids come from an atomic counter, so a tile only ever waits on
