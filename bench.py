@@ -18,9 +18,11 @@ twentieth (at least one) of the timed steps, inside the same timed region
 (recording them in every step would add about 2 us per launch to the time per
 step).  Algorithmic bytes: 16 B per key per pass for key-value sorts (read and
 write key and value), 8 B for keys-only sorts, 8 B per element for compaction
-(read the input, write the output including the zero tail).  The CPU baseline
-is the oracle (single-threaded C) on a bounded prefix of the same workload.
---all prints one line per workload (the default line first).
+(read the input, write the output including the zero tail).  The default line also
+carries "keys_u32_2p28": the keys-only sort of the same 2^28 keys, timed the
+same way.  The CPU baseline is the oracle (single-threaded C) on the same
+workload, repeated for about 10 s.  --all prints one line per workload (the
+default line first).
 """
 import argparse
 import hashlib
@@ -83,12 +85,35 @@ def make_inputs(name):
     return keys, (vals if kind != "keys_u32" else None)
 
 
-def cpu_baseline(name, keys, vals, budget_s=12.0, sample=1 << 24):
-    """The oracle on the first `sample` elements, repeated up to about budget_s."""
+def host_cpu():
+    """(usable cores, model name) of the host this runs on."""
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    model = "unknown"
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
+    return cores, model
+
+
+def cpu_baseline(name, keys, vals, budget_s=10.0, sample=None):
+    """The oracle on the workload (or its first `sample` elements), repeated
+    until about budget_s of CPU time has been spent."""
     import oracle
     _, kind, n, b, e = WORKLOADS[name]
-    k = keys[:sample].copy()
-    v = vals[:sample].copy() if vals is not None else None
+    if sample is None or sample >= keys.size:
+        k, v, what = keys, vals, "the whole workload (%d elements)" % keys.size
+    else:
+        k = keys[:sample].copy()
+        v = vals[:sample].copy() if vals is not None else None
+        what = "the first %d elements of the workload" % sample
     runs, total = 0, 0.0
     while True:
         t0 = time.perf_counter()
@@ -102,13 +127,81 @@ def cpu_baseline(name, keys, vals, budget_s=12.0, sample=1 << 24):
             oracle.sort_u32(k, v, b, e)
         total += time.perf_counter() - t0
         runs += 1
-        if total >= budget_s or runs >= (1000 if k.size <= 4096 else 5):
+        if total >= budget_s or runs >= (1000 if k.size <= 4096 else 50):
             break
     per_run = total / runs
     unit = "G elements/s" if kind == "compact" else "Gkeys/s"
+    host_cores, model = host_cpu()
     return {"value": round(k.size / per_run / 1e9, 6), "unit": unit, "cores": 1, "kind": "oracle",
-            "sample": "first %d elements of the same workload, %d run(s), %.4f s each; "
-                      "single-threaded C oracle (gcc -O2)" % (k.size, runs, per_run)}
+            "sample": "%s, %d run(s), %.4f s each; single-threaded C oracle (gcc -O2)"
+                      % (what, runs, per_run),
+            "host_cores": host_cores, "host_cpu": model}
+
+
+def timed_region(step, steps, warmup, stream):
+    """Time `steps` calls of step() between two events on `stream`.
+
+    The library's per-launch events are recorded only during the last
+    `event_steps` calls: each event still adds about 2 us between launches,
+    which would otherwise inflate the time per step of small sorts by up to a
+    third.  Returns (ms per step, {kernel: [ms per launch]}, event_steps)."""
+    import torch
+
+    import sorting_lsd_radix_amd as rs
+    for _ in range(warmup):
+        step()
+    torch.cuda.synchronize()
+    event_steps = max(1, steps // 20)
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    start.record(stream)
+    for i in range(steps):
+        if i == steps - event_steps:
+            rs.rs_timing_enable(True)
+        step()
+    stop.record(stream)
+    torch.cuda.synchronize()
+    total_ms = start.elapsed_time(stop)
+    records = rs.rs_timing_collect()
+    rs.rs_timing_enable(False)
+    per_kernel = {}
+    for kname, ms in records:
+        per_kernel.setdefault(kname, []).append(ms)
+    return total_ms / steps, per_kernel, event_steps
+
+
+def keys_only_companion(kin, n, steps, warmup, stream, pairs_keys_out, check):
+    """The keys-only half of the metric on the same device keys: one whole
+    rs_sort_keys_u32 call per step (fill, upsweep, 4 passes)."""
+    import numpy as np
+    import torch
+
+    import sorting_lsd_radix_amd as rs
+    kout = torch.empty_like(kin)
+    need = rs.rs_sort_keys_u32(None, None, n, 0, 32, None, 0)
+    temp = torch.empty(max(need, 1), dtype=torch.uint8, device=kin.device)
+
+    def step():
+        rs.rs_sort_keys_u32(kin, kout, n, 0, 32, temp, need, stream)
+
+    ms, per_kernel, _ = timed_region(step, steps, warmup, stream)
+    print("bench: keys_u32_2p28 timed %d steps, %.4f ms/step" % (steps, ms), file=sys.stderr,
+          flush=True)
+    if check:
+        # the keys of the checked pair sort are the sorted keys: the keys-only
+        # output must equal them
+        if not torch.equal(kout, pairs_keys_out):
+            print("bench: OUTPUT CHECK FAILED for keys_u32_2p28", file=sys.stderr, flush=True)
+            sys.exit(1)
+    pass_ms = per_kernel.get("onesweep", [float("nan")])
+    pass_ms = sum(pass_ms) / len(pass_ms)
+    return {"workload": WORKLOADS["keys_u32_2p28"][0], "value": round(n / (ms * 1e-3) / 1e9, 4),
+            "unit": "Gkeys/s", "ms_per_step": round(ms, 5),
+            "pass_ms": round(pass_ms, 5),
+            "pass_roofline_frac": round(8 * n / (pass_ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "whole_step_roofline_frac": round(8 * n * 4 / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()}}
 
 
 def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
@@ -160,35 +253,9 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         torch.cuda.synchronize()
         del a, c
 
-    for _ in range(warmup):
-        step()
-    torch.cuda.synchronize()
-
-    # One timed region of `steps` calls.  The library's per-launch events are
-    # recorded only during its last `event_steps` calls: each event still
-    # adds about 2 us between launches, which would otherwise inflate the
-    # time per step of small sorts by up to a third.
-    event_steps = max(1, steps // 20)
-    start = torch.cuda.Event(enable_timing=True)
-    stop = torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    start.record(stream)
-    for i in range(steps):
-        if i == steps - event_steps:
-            rs.rs_timing_enable(True)
-        step()
-    stop.record(stream)
-    torch.cuda.synchronize()
-    total_ms = start.elapsed_time(stop)
-    records = rs.rs_timing_collect()
-    rs.rs_timing_enable(False)
-    ms_per_step = total_ms / steps
+    ms_per_step, per_kernel, event_steps = timed_region(step, steps, warmup, stream)
     print("bench: %s timed %d steps, %.4f ms/step" % (name, steps, ms_per_step), file=sys.stderr,
           flush=True)
-
-    per_kernel = {}
-    for kname, ms in records:
-        per_kernel.setdefault(kname, []).append(ms)
 
     if check:
         ok = True
@@ -282,6 +349,9 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         "whole_step_roofline_frac": round(algo_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()},
     }
+    if name == DEFAULT:
+        # the metric names keys-only sorts as well: same keys, same step count
+        result["keys_u32_2p28"] = keys_only_companion(kin, n, steps, warmup, stream, kout, check)
     result["cpu_baseline"] = cpu_baseline(name, keys, vals) if with_cpu else None
     return result
 

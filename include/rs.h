@@ -35,6 +35,15 @@
  *    affects speed, never results.
  *  - n < 2^30 (RS_ERR_UNSUPPORTED_SIZE otherwise): cross-tile prefix states
  *    hold 30-bit counts beside 2 status bits.
+ *  - Scheduling assumption of the persistent kernels (sort passes and
+ *    compaction): their grid never exceeds the number of blocks that fit on
+ *    the device at once, tiles are handed out in increasing order per group
+ *    of blocks, and a tile waits only on tiles with smaller ids.  Progress
+ *    needs at least one block of every group (up to 8) to be resident, which
+ *    holds whenever the kernel can start on the device at all (other work on
+ *    other streams only delays blocks that have not started; blocks that
+ *    started keep running).  A device partitioned so that a kernel's blocks
+ *    could be preempted indefinitely is outside this contract.
  */
 #ifndef RS_H
 #define RS_H

@@ -9,7 +9,9 @@ storage with torch on the tensors' device and launch on torch's current
 stream; torch provides memory and streams only.
 
 Loading fails with an error when ``librs.so`` has not been built; there is no
-fallback implementation.
+fallback implementation.  ``use_library(path)`` binds the functions to another
+build of the same sources (the tests use it for the build with the ballot rank
+forced on every path, ``librs_ballot.so``).
 """
 import ctypes
 import os
@@ -20,7 +22,7 @@ __all__ = [
     "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_compact_positive_f32",
     "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
     "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "compact_positive_f32", "bitonic_tile",
-    "library_path", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
+    "library_path", "use_library", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
 ]
 
 _PKG = os.path.dirname(os.path.abspath(__file__))
@@ -50,6 +52,7 @@ EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32"
                     "rs_timing_enable", "rs_timing_collect"]
 
 _lib = None
+_lib_path = _LIB_PATH
 
 
 class RsError(RuntimeError):
@@ -59,18 +62,28 @@ class RsError(RuntimeError):
 
 
 def library_path():
-    return _LIB_PATH
+    return _lib_path
+
+
+def use_library(path=None):
+    """Bind every function to the library at `path` (None: the default
+    librs.so); returns the previous path."""
+    global _lib, _lib_path
+    prev = _lib_path
+    _lib_path = _LIB_PATH if path is None else os.path.abspath(path)
+    _lib = None
+    return prev
 
 
 def _load():
     global _lib
     if _lib is not None:
         return _lib
-    if not os.path.exists(_LIB_PATH):
-        raise RuntimeError("librs.so is not built (%s); run "
+    if not os.path.exists(_lib_path):
+        raise RuntimeError("%s is not built; run "
                            "`python -m sorting_lsd_radix_amd.build` or "
-                           "`python -c 'import __graft_entry__ as g; g.build()'`" % _LIB_PATH)
-    lib = ctypes.CDLL(_LIB_PATH)
+                           "`python -c 'import __graft_entry__ as g; g.build()'`" % _lib_path)
+    lib = ctypes.CDLL(_lib_path)
     vp, u64, i32, u32 = ctypes.c_void_p, ctypes.c_uint64, ctypes.c_int, ctypes.c_uint32
     szp = ctypes.POINTER(ctypes.c_size_t)
     lib.rs_sort_keys_u32.argtypes = [vp, vp, u64, i32, i32, vp, szp, vp]

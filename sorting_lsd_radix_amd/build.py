@@ -21,15 +21,36 @@ FLAGS = [
 ]
 
 
-def build(verbose=False, extra_flags=()):
-    """Compile every source into librs.so (always recompiles)."""
+# The same sources built with the ballot rank forced on every path (the
+# library's default ranks with LDS atomics whose same-address lanes gfx950
+# serves in lane order); the GPU tests run a parity subset against it.
+BALLOT_LIB_PATH = os.path.join(PKG, "librs_ballot.so")
+BALLOT_FLAGS = ["-DRS_FORCE_BALLOT_RANK"]
+
+
+def compile_library(out, extra_flags=(), verbose=False):
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB_PATH + ".tmp"
+    tmp = out + ".tmp"
     cmd = [HIPCC] + FLAGS + list(extra_flags) + ["-I", INCLUDE, "-I", CSRC, "-o", tmp] + srcs
     if verbose:
         print(" ".join(cmd), flush=True)
     subprocess.run(cmd, check=True)
-    os.replace(tmp, LIB_PATH)
+    os.replace(tmp, out)
+    return out
+
+
+def build(verbose=False, extra_flags=(), ballot_variant=True):
+    """Compile every source into librs.so (always recompiles), and the
+    forced-ballot variant librs_ballot.so beside it."""
+    jobs = [(LIB_PATH, list(extra_flags))]
+    if ballot_variant:
+        jobs.append((BALLOT_LIB_PATH, list(extra_flags) + BALLOT_FLAGS))
+    if len(jobs) == 1:
+        return compile_library(LIB_PATH, extra_flags, verbose)
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(len(jobs)) as ex:
+        for f in [ex.submit(compile_library, out, fl, verbose) for out, fl in jobs]:
+            f.result()
     return LIB_PATH
 
 

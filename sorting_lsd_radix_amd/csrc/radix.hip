@@ -200,6 +200,19 @@ __device__ __forceinline__ uint64_t lanes_with_other_digit(uint32_t d) {
     return (static_cast<uint64_t>(diff_hi) << 32) | diff_lo;
 }
 
+// Ballot rank of one row: the wave's running count of digit d plus the lanes
+// below this one that hold the same digit; the lowest lane of each digit group
+// advances the wave's counter by the group's size.  LDS instructions of one
+// wave execute in order, so the next row reads the advanced counters.
+__device__ __forceinline__ uint32_t ballot_rank(uint32_t* my_count, uint32_t d, uint32_t lane) {
+    const uint32_t before = my_count[d];
+    const uint64_t others = lanes_with_other_digit(d);
+    const uint32_t below = lane - count_below(others);      // same digit, lower lane
+    const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
+    if (below == 0) my_count[d] = before + group_size;
+    return before + below;
+}
+
 // Arguments of one digit pass.
 struct PassArgs {
     const uint32_t* src_keys;
@@ -219,9 +232,12 @@ struct PassArgs {
 // Loads the ITEMS keys of this lane for `tile`: row j of wave w is the 64
 // consecutive keys at tile*TILE + w*64*ITEMS + j*64.  The loads go through a
 // buffer descriptor of n elements, so a row past the end of a partial tile
-// reads 0 without a branch or a clamp (the padding is applied afterwards);
-// they are non-temporal, since each key is read once per pass.  The row
-// offsets fold into the instructions' immediate offsets.
+// reads 0 without a branch or a clamp (the padding is applied afterwards;
+// where the tile reaches past 2^30 keys such a row's byte offset wraps round
+// 2^32 and reads keys from the start of the same buffer, which are replaced
+// by the padding and never stored); they are non-temporal, since each key is
+// read once per pass.  The row offsets fold into the instructions'
+// immediate offsets.
 template <int ITEMS, int TILE>
 __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint32_t tile,
                                           uint32_t n, uint32_t wave, uint32_t lane,
@@ -276,7 +292,11 @@ void onesweep_kernel(PassArgs a) {
     // pass's keys, and for a tile only if the block's previous tile had no
     // digit over that share of its keys (earlier passes gather equal keys
     // into runs, which then collide within a row); otherwise the ballot rank.
+#ifdef RS_FORCE_BALLOT_RANK
+    const bool spread = false;   // build switch: ballot rank on every tile
+#else
     const bool spread = !__syncthreads_or((static_cast<uint64_t>(bin) << a.atomic_limit_log2) > n);
+#endif
     bool atomic_rank = spread;   // uniform
 
     for (;;) {
@@ -331,13 +351,9 @@ void onesweep_kernel(PassArgs a) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
-                const uint32_t before = my_count[d];
-                const uint64_t others = lanes_with_other_digit(d);
-                const uint32_t below = lane - count_below(others);      // same digit, lower lane
-                const uint32_t group_size = kWave - static_cast<uint32_t>(__popcll(others));
-                if (below == 0) my_count[d] = before + group_size;
-                if (j % 2 == 0) pos[j / 2] = before + below;
-                else pos[j / 2] |= (before + below) << 16;
+                const uint32_t slot = ballot_rank(my_count, d, lane);
+                if (j % 2 == 0) pos[j / 2] = slot;
+                else pos[j / 2] |= slot << 16;
                 // the slots are chained through the LDS counters anyway; keeping the
                 // scheduler from interleaving them keeps register pressure low
                 __builtin_amdgcn_sched_barrier(0);
@@ -472,7 +488,9 @@ void onesweep_kernel(PassArgs a) {
         // store past the end, which is where every pad of a partial tile
         // lands (pads rank after the last real key of the last digit, whose
         // run ends at n), so no slot needs a branch and the LDS reads of all
-        // slots can be in flight together.
+        // slots can be in flight together.  A pad's destination can lie past
+        // 2^30, where its byte offset would wrap round 2^32 back into the
+        // buffer; it is clamped to n first (n * 4 < 2^32 is out of range).
         const __amdgpu_buffer_rsrc_t out_keys =
             __builtin_amdgcn_make_buffer_rsrc(dst_keys, 0, static_cast<int>(n * 4u), kBufferWord3);
         uint32_t digits[PAIRS ? ITEMS / 4 : 1];
@@ -485,7 +503,7 @@ void onesweep_kernel(PassArgs a) {
                 if (r % 4 == 0) digits[r / 4] = d;
                 else digits[r / 4] |= d << (8 * (r % 4));
             }
-            const uint32_t dst = i + s_adjust[d];
+            const uint32_t dst = min(i + s_adjust[d], n);
             __builtin_amdgcn_raw_buffer_store_b32(FLIP_OUT ? sortable_to_float(key) : key, out_keys,
                                                   static_cast<int>(dst * 4u), 0, 0);
             if (PAIRS && r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounds live registers
@@ -501,7 +519,7 @@ void onesweep_kernel(PassArgs a) {
             for (int r = 0; r < ITEMS; ++r) {
                 const uint32_t i = r * BLOCK + tid;
                 const uint32_t d = (digits[r / 4] >> (8 * (r % 4))) & 0xFFu;
-                const uint32_t dst = i + s_adjust[d];
+                const uint32_t dst = min(i + s_adjust[d], n);
                 __builtin_amdgcn_raw_buffer_store_b32(s_buf[i], out_vals, static_cast<int>(dst * 4u), 0, 0);
             }
         }
@@ -563,13 +581,17 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
         // Stable rank with one LDS atomic add per key (same-address lanes of
         // one instruction are served in lane order on gfx950, as in the
         // one-sweep pass; at these sizes the serialisation of crowded digits
-        // costs little, so no ballot fallback).
+        // costs little, so no ballot fallback unless the build forces it).
         uint32_t pos[ITEMS / 2];
         uint32_t* my_count = s_off + wave * kRadix;
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+#ifdef RS_FORCE_BALLOT_RANK
+            const uint32_t slot = ballot_rank(my_count, d, lane);
+#else
             const uint32_t slot = atomicAdd(&my_count[d], 1u);   // served in lane order
+#endif
             if (j % 2 == 0) pos[j / 2] = slot;
             else pos[j / 2] |= slot << 16;
         }

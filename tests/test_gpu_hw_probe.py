@@ -1,11 +1,16 @@
-"""GPU check of the hardware property the large keys-only pass relies on.
+"""GPU check of the hardware property the stable rank of the sort relies on.
 
-The 512 x 32 keys-only pass ranks each key with one LDS atomic add
-(`ds_add_rtn_u32`) on its wave's digit counter.  That rank is the stable one
-only if the lanes of one instruction that hit the same counter are served in
-lane order.  This test runs a probe kernel (tests/hw_probe/lds_lane_order.hip)
-that compares every atomic result with the lane-order rank, for uniform,
-clustered, all-equal, skewed and same-bank digit patterns.
+Every one-sweep pass kernel (keys only and key-value, every tile shape, u32
+and float keys) ranks a key with one LDS atomic add (`ds_add_rtn_u32`) on its
+wave's digit counter while the digits of the pass are spread out, and the
+one-workgroup sort of up to 16384 keys always does.  That rank is the stable
+one only if the lanes of one instruction that hit the same counter are
+served in lane order: observed gfx950 behaviour, not a documented guarantee.
+This test runs a probe kernel (tests/hw_probe/lds_lane_order.hip) that
+compares every atomic result with the lane-order rank, for uniform,
+clustered, all-equal, skewed and same-bank digit patterns.  The library can
+be built with the ballot rank forced on every path (RS_FORCE_BALLOT_RANK),
+which does not depend on this property.
 """
 import ctypes
 import os

@@ -295,20 +295,27 @@ def test_workload_float_pairs_2p28():
     for pattern in (workloads.SUBNORMAL_NEG_BITS, 0x80000000, 0x00000000,
                     workloads.SUBNORMAL_POS_BITS):
         assert int((kb == np.uint32(pattern)).sum()) >= m
+    print("float pairs 2^28 oracle", flush=True)
+    rk, rv = oracle.sort_f32(keys, vals)
+    assert np.array_equal(v, rv), "values differ from the oracle"
+    assert np.array_equal(kb, rk.view(np.uint32)), "keys differ from the oracle"
 
 
 def test_workload_headline_pairs_and_keys_2p28():
-    """2^28 uniform pairs (and the keys-only sort of the same keys)."""
+    """2^28 uniform pairs and the keys-only sort of the same keys, both
+    compared element by element with the oracle."""
     print("headline 2^28 generate", flush=True)
     keys, vals = workloads.headline_pairs()
     k, v = gpu_sort_pairs_u32(keys, vals)
     print("headline 2^28 check", flush=True)
     check_stable_sort_by_order(keys, k, k, v)
-    del v
+    print("headline 2^28 oracle (pairs)", flush=True)
+    rk, rv = oracle.sort_u32(keys, vals)
+    assert np.array_equal(v, rv), "values differ from the oracle"
+    assert np.array_equal(k, rk), "keys differ from the oracle"
+    del v, rv, k
+    print("headline 2^28 keys only", flush=True)
     ko = gpu_sort_keys_u32(keys)
-    assert np.array_equal(ko, k)
-    # a sample of ranks recomputed by the oracle's own sort of a key slice
-    sample = keys[:1 << 16]
-    rk = oracle.sort_u32(sample)
-    pos = np.searchsorted(k, rk, side="left")
-    assert np.array_equal(k[pos], rk)
+    print("headline 2^28 oracle (keys)", flush=True)
+    assert np.array_equal(ko, oracle.sort_u32(keys)), "keys-only sort differs from the oracle"
+    assert np.array_equal(ko, rk)
