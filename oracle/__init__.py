@@ -92,6 +92,15 @@ class Oracle:
         lib.oracle_f32_to_order.restype = None
         lib.oracle_order_to_f32.argtypes = [_U32P, _U32P, u64]
         lib.oracle_order_to_f32.restype = None
+        vp = ctypes.c_void_p
+        lib.oracle_lsd_sort_u64.argtypes = [_U64P, _U32P, _U64P, _U32P, u64, i32, i32, i32]
+        lib.oracle_lsd_sort_u64.restype = i32
+        lib.oracle_sort_typed.argtypes = [i32, i32, vp, _U32P, vp, _U32P, u64, i32, i32, i32]
+        lib.oracle_sort_typed.restype = i32
+        lib.oracle_digit_histograms_typed.argtypes = [i32, i32, vp, u64, i32, i32, _U64P]
+        lib.oracle_digit_histograms_typed.restype = i32
+        lib.oracle_sort_two_keys.argtypes = [_U32P, _U32P, _U32P, _U32P, _U32P, _U32P, u64]
+        lib.oracle_sort_two_keys.restype = i32
         self.lib = lib
         self.path = path
 
@@ -187,6 +196,98 @@ class Oracle:
         return out
 
 
+    # ---- key types, 64-bit keys, multi-key --------------------------------------
+
+    def sort_u64(self, keys, vals=None, begin_bit=0, end_bit=64, digit_bits=8):
+        """Stable LSD radix sort of uint64 keys by bits [begin_bit, end_bit)."""
+        keys = np.ascontiguousarray(keys)
+        if keys.dtype != np.uint64:
+            raise TypeError("expected uint64 keys, got %s" % keys.dtype)
+        n = keys.size
+        k_out = np.empty(n, np.uint64)
+        v_out = None
+        vp = None
+        if vals is not None:
+            vals = _u32(vals)
+            if vals.size != n:
+                raise ValueError("keys and vals differ in length")
+            v_out = np.empty(n, np.uint32)
+            vp = _ptr(vals, ctypes.c_uint32)
+        _check(self.lib.oracle_lsd_sort_u64(_ptr(keys, ctypes.c_uint64), vp,
+                                            _ptr(k_out, ctypes.c_uint64),
+                                            _ptr(v_out, ctypes.c_uint32),
+                                            n, begin_bit, end_bit, digit_bits),
+               "oracle_lsd_sort_u64")
+        return k_out if vals is None else (k_out, v_out)
+
+    def sort_typed(self, keys, vals=None, begin_bit=0, end_bit=None, descending=False,
+                   digit_bits=8):
+        """Stable sort of a uint32/int32/float32/uint64/int64/float64 array by
+        bits [begin_bit, end_bit) of its order pattern (end_bit defaults to the
+        key width), ascending or descending; returns keys or (keys, vals)."""
+        keys = np.ascontiguousarray(keys)
+        key_type = KEY_TYPES[keys.dtype.type]
+        width = keys.dtype.itemsize * 8
+        end_bit = width if end_bit is None else end_bit
+        n = keys.size
+        k_out = np.empty_like(keys)
+        v_out = None
+        vp = None
+        if vals is not None:
+            vals = _u32(vals)
+            if vals.size != n:
+                raise ValueError("keys and vals differ in length")
+            v_out = np.empty(n, np.uint32)
+            vp = _ptr(vals, ctypes.c_uint32)
+        _check(self.lib.oracle_sort_typed(key_type, int(bool(descending)), keys.ctypes.data, vp,
+                                          k_out.ctypes.data, _ptr(v_out, ctypes.c_uint32), n,
+                                          begin_bit, end_bit, digit_bits),
+               "oracle_sort_typed")
+        return k_out if vals is None else (k_out, v_out)
+
+    def digit_histograms_typed(self, keys, begin_bit=0, end_bit=None, descending=False):
+        """counts[p, d] of the order patterns of typed keys (uint64)."""
+        keys = np.ascontiguousarray(keys)
+        key_type = KEY_TYPES[keys.dtype.type]
+        end_bit = keys.dtype.itemsize * 8 if end_bit is None else end_bit
+        passes = (end_bit - begin_bit + 7) // 8
+        out = np.zeros(max(passes, 1) * 256, np.uint64)
+        p = _check(self.lib.oracle_digit_histograms_typed(key_type, int(bool(descending)),
+                                                          keys.ctypes.data, keys.size, begin_bit,
+                                                          end_bit, _ptr(out, ctypes.c_uint64)),
+                   "oracle_digit_histograms_typed")
+        return out[: p * 256].reshape(p, 256)
+
+    def sort_two_keys(self, first, second, vals=None):
+        """Stable sort by `first`, then stable sort of that by `second` (the
+        multi-key exercise); returns (first, second) or (first, second, vals)
+        permuted."""
+        first, second = _u32(first), _u32(second)
+        n = first.size
+        if second.size != n:
+            raise ValueError("keys differ in length")
+        f_out = np.empty(n, np.uint32)
+        s_out = np.empty(n, np.uint32)
+        v_out = None
+        if vals is not None:
+            vals = _u32(vals)
+            if vals.size != n:
+                raise ValueError("keys and vals differ in length")
+            v_out = np.empty(n, np.uint32)
+        _check(self.lib.oracle_sort_two_keys(_ptr(first, ctypes.c_uint32),
+                                             _ptr(second, ctypes.c_uint32),
+                                             _ptr(vals, ctypes.c_uint32),
+                                             _ptr(f_out, ctypes.c_uint32),
+                                             _ptr(s_out, ctypes.c_uint32),
+                                             _ptr(v_out, ctypes.c_uint32), n),
+               "oracle_sort_two_keys")
+        return (f_out, s_out) if vals is None else (f_out, s_out, v_out)
+
+
+# numpy scalar type -> key type code of oracle_sort_typed (the library uses
+# the same numbering)
+KEY_TYPES = {np.uint32: 0, np.int32: 1, np.float32: 2, np.uint64: 3, np.int64: 4, np.float64: 5}
+
 _default = None
 
 
@@ -224,3 +325,19 @@ def f32_to_order(*a, **k):
 
 def order_to_f32(*a, **k):
     return default().order_to_f32(*a, **k)
+
+
+def sort_u64(*a, **k):
+    return default().sort_u64(*a, **k)
+
+
+def sort_typed(*a, **k):
+    return default().sort_typed(*a, **k)
+
+
+def digit_histograms_typed(*a, **k):
+    return default().digit_histograms_typed(*a, **k)
+
+
+def sort_two_keys(*a, **k):
+    return default().sort_two_keys(*a, **k)

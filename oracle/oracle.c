@@ -40,6 +40,28 @@
  *    (field, original index) pairs -- the form used on the GPU because the
  *    network itself is not stable ("第10章", 10.7 稳定排序 vs 不稳定排序) --
  *    reaches exactly this result, so the oracle is the definition.
+ *  - oracle_lsd_sort_u64: the same digit-by-digit stable counting sort on
+ *    64-bit keys; with 8-bit digits a full 64-bit key takes eight passes
+ *    ("第10章", 八、习题: the exercise on iteration counts for 64-bit
+ *    integers).
+ *  - oracle_sort_typed: keys of six types (u32, i32, f32, u64, i64, f64),
+ *    ascending or descending, with optional u32 values.  Each key is mapped
+ *    to an unsigned "order pattern" whose unsigned order is the type's
+ *    order: unsigned keys as they are, signed keys offset by 2^(w-1)
+ *    (two's complement values -2^(w-1) .. 2^(w-1)-1 onto 0 .. 2^w-1), floats
+ *    by the sign-dependent transform above (the float exercise of 八、习题);
+ *    descending order replaces the pattern p by its complement 2^w - 1 - p
+ *    (the exercise on descending sorts), which reverses the order and keeps
+ *    equal keys equal, so the sort stays stable.  The bit range selects bits
+ *    of that pattern.  The oracle sorts (pattern, original index) with the
+ *    LSD sort and then gathers the original keys and values by index, so it
+ *    never needs an inverse transform.
+ *  - oracle_sort_two_keys: the multi-key exercise of 八、习题 done as the
+ *    exercise states it: a stable sort by the first key, then a stable sort
+ *    of that result by the second key.  The result is ordered by the second
+ *    key, then by the first, then by input position.
+ *  - oracle_digit_histograms_typed: per-pass digit counts of the order
+ *    patterns of any of the six key types (up to eight passes).
  *
  * Floating point: the compaction predicate is the C comparison x > 0.0f on
  * the float value, as the pages write it.  This file must be built without
@@ -282,4 +304,285 @@ int oracle_bitonic_tile(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n,
             return rc;
     }
     return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* 64-bit keys, key types and multi-key sorts                                */
+/* ------------------------------------------------------------------------ */
+
+/* The digit of a 64-bit key that starts at bit `shift` and is `width` bits wide. */
+static uint64_t digit_at64(uint64_t key, int shift, int width)
+{
+    uint64_t low_bits = (width >= 64) ? ~(uint64_t)0 : (((uint64_t)1 << width) - 1);
+    return (key >> shift) & low_bits;
+}
+
+/* One stable counting-sort pass of 64-bit keys (values optional). */
+static void counting_sort_pass64(const uint64_t *src_keys, const uint32_t *src_vals,
+                                 uint64_t *dst_keys, uint32_t *dst_vals, uint64_t n,
+                                 int shift, int width, uint64_t *cnt)
+{
+    uint64_t buckets = (uint64_t)1 << width;
+    uint64_t d, j, running;
+
+    for (d = 0; d < buckets; ++d)
+        cnt[d] = 0;
+    for (j = 0; j < n; ++j)
+        cnt[digit_at64(src_keys[j], shift, width)] += 1;
+    /* exclusive scan: cnt[d] becomes the first output slot of digit d */
+    running = 0;
+    for (d = 0; d < buckets; ++d) {
+        uint64_t here = cnt[d];
+        cnt[d] = running;
+        running += here;
+    }
+    /* scatter in input order */
+    for (j = 0; j < n; ++j) {
+        uint64_t dg = digit_at64(src_keys[j], shift, width);
+        uint64_t at = cnt[dg]++;
+        dst_keys[at] = src_keys[j];
+        if (src_vals)
+            dst_vals[at] = src_vals[j];
+    }
+}
+
+/*
+ * Stable LSD radix sort of 64-bit keys (with optional u32 values) by bits
+ * [begin_bit, end_bit), 0 <= begin_bit <= end_bit <= 64, digits of
+ * `digit_bits` bits (1..16), the last one narrowed.
+ */
+int oracle_lsd_sort_u64(const uint64_t *keys_in, const uint32_t *vals_in,
+                        uint64_t *keys_out, uint32_t *vals_out, uint64_t n,
+                        int begin_bit, int end_bit, int digit_bits)
+{
+    uint64_t *ka, *kb, *tk, *cnt;
+    uint32_t *va = NULL, *vb = NULL, *tv;
+    int shift;
+    int pairs = (vals_in != NULL);
+
+    if (begin_bit < 0 || end_bit > 64 || begin_bit > end_bit)
+        return ORACLE_BAD_ARGS;
+    if (digit_bits < 1 || digit_bits > 16)
+        return ORACLE_BAD_ARGS;
+    if ((vals_in == NULL) != (vals_out == NULL))
+        return ORACLE_BAD_ARGS;
+    if (n == 0)
+        return ORACLE_OK;
+
+    ka = (uint64_t *)malloc(n * sizeof(uint64_t));
+    kb = (uint64_t *)malloc(n * sizeof(uint64_t));
+    cnt = (uint64_t *)malloc(((size_t)1 << digit_bits) * sizeof(uint64_t));
+    if (pairs) {
+        va = (uint32_t *)malloc(n * sizeof(uint32_t));
+        vb = (uint32_t *)malloc(n * sizeof(uint32_t));
+    }
+    if (!ka || !kb || !cnt || (pairs && (!va || !vb))) {
+        free(ka); free(kb); free(cnt); free(va); free(vb);
+        return ORACLE_NO_MEMORY;
+    }
+    memcpy(ka, keys_in, n * sizeof(uint64_t));
+    if (pairs)
+        memcpy(va, vals_in, n * sizeof(uint32_t));
+
+    for (shift = begin_bit; end_bit > shift; shift += digit_bits) {
+        /* the last digit keeps only the bits left in the range */
+        int width = (end_bit - shift < digit_bits) ? end_bit - shift : digit_bits;
+        counting_sort_pass64(ka, va, kb, vb, n, shift, width, cnt);
+        tk = ka; ka = kb; kb = tk;
+        tv = va; va = vb; vb = tv;
+    }
+
+    memcpy(keys_out, ka, n * sizeof(uint64_t));
+    if (pairs)
+        memcpy(vals_out, va, n * sizeof(uint32_t));
+    free(ka); free(kb); free(cnt); free(va); free(vb);
+    return ORACLE_OK;
+}
+
+/* Key types of oracle_sort_typed (the same numbering as the library's). */
+#define ORACLE_KEY_U32 0
+#define ORACLE_KEY_I32 1
+#define ORACLE_KEY_F32 2
+#define ORACLE_KEY_U64 3
+#define ORACLE_KEY_I64 4
+#define ORACLE_KEY_F64 5
+
+static int key_bits_of(int key_type)
+{
+    if (key_type >= ORACLE_KEY_U32 && key_type <= ORACLE_KEY_F32)
+        return 32;
+    if (key_type >= ORACLE_KEY_U64 && key_type <= ORACLE_KEY_F64)
+        return 64;
+    return 0;
+}
+
+/*
+ * The order pattern of key i (see the header): unsigned, w = 32 or 64 bits,
+ * such that comparing patterns as unsigned integers compares the keys.
+ */
+static uint64_t order_pattern(int key_type, int descending, const void *keys, uint64_t i)
+{
+    uint64_t p = 0, top;
+    int w = key_bits_of(key_type);
+    uint64_t all = (w == 64) ? ~(uint64_t)0 : (uint64_t)0xFFFFFFFFu;
+
+    switch (key_type) {
+    case ORACLE_KEY_U32:
+        p = ((const uint32_t *)keys)[i];
+        break;
+    case ORACLE_KEY_I32:
+        /* value + 2^31, as an unsigned 32-bit number */
+        p = (uint64_t)((int64_t)((const int32_t *)keys)[i] + ((int64_t)1 << 31));
+        break;
+    case ORACLE_KEY_F32:
+        p = f32_to_order(((const uint32_t *)keys)[i]);
+        break;
+    case ORACLE_KEY_U64:
+        p = ((const uint64_t *)keys)[i];
+        break;
+    case ORACLE_KEY_I64:
+        /* value + 2^63 modulo 2^64: the two's complement pattern plus 2^63 */
+        p = ((const uint64_t *)keys)[i] + ((uint64_t)1 << 63);
+        break;
+    case ORACLE_KEY_F64:
+        top = (uint64_t)1 << 63;
+        p = ((const uint64_t *)keys)[i];
+        p = (p & top) ? ~p : (p | top);
+        break;
+    }
+    if (descending)
+        p = all - p;
+    return p;
+}
+
+/*
+ * Stable sort of keys of `key_type` (ascending, or descending when
+ * `descending` is nonzero) by bits [begin_bit, end_bit) of their order
+ * patterns, with optional u32 values; keys_out receives the original keys.
+ * Keys are u32/i32/f32 arrays (4 bytes each) or u64/i64/f64 arrays (8 bytes).
+ */
+int oracle_sort_typed(int key_type, int descending, const void *keys_in,
+                      const uint32_t *vals_in, void *keys_out, uint32_t *vals_out,
+                      uint64_t n, int begin_bit, int end_bit, int digit_bits)
+{
+    uint64_t *pat, *pat_sorted, i;
+    uint32_t *idx, *idx_sorted;
+    int w = key_bits_of(key_type);
+    int rc;
+
+    if (w == 0 || begin_bit < 0 || end_bit > w || begin_bit > end_bit)
+        return ORACLE_BAD_ARGS;
+    if ((vals_in == NULL) != (vals_out == NULL))
+        return ORACLE_BAD_ARGS;
+    if (n == 0)
+        return ORACLE_OK;
+    if (n > 0xFFFFFFFFu)
+        return ORACLE_BAD_ARGS;
+
+    pat = (uint64_t *)malloc(n * sizeof(uint64_t));
+    pat_sorted = (uint64_t *)malloc(n * sizeof(uint64_t));
+    idx = (uint32_t *)malloc(n * sizeof(uint32_t));
+    idx_sorted = (uint32_t *)malloc(n * sizeof(uint32_t));
+    if (!pat || !pat_sorted || !idx || !idx_sorted) {
+        free(pat); free(pat_sorted); free(idx); free(idx_sorted);
+        return ORACLE_NO_MEMORY;
+    }
+    for (i = 0; i < n; ++i) {
+        pat[i] = order_pattern(key_type, descending, keys_in, i);
+        idx[i] = (uint32_t)i;
+    }
+    rc = oracle_lsd_sort_u64(pat, idx, pat_sorted, idx_sorted, n, begin_bit, end_bit,
+                             digit_bits);
+    if (rc == ORACLE_OK) {
+        for (i = 0; i < n; ++i) {
+            uint64_t src = idx_sorted[i];
+            if (w == 32)
+                ((uint32_t *)keys_out)[i] = ((const uint32_t *)keys_in)[src];
+            else
+                ((uint64_t *)keys_out)[i] = ((const uint64_t *)keys_in)[src];
+            if (vals_in)
+                vals_out[i] = vals_in[src];
+        }
+    }
+    free(pat); free(pat_sorted); free(idx); free(idx_sorted);
+    return rc;
+}
+
+/*
+ * Per-pass 8-bit digit counts of the order patterns of `key_type` keys over
+ * bits [begin_bit, end_bit) (passes = ceil((end - begin) / 8) <= 8):
+ * counts[p * 256 + d].  Returns the pass count, or a negative code.
+ */
+int oracle_digit_histograms_typed(int key_type, int descending, const void *keys, uint64_t n,
+                                  int begin_bit, int end_bit, uint64_t *counts)
+{
+    int passes, p, w = key_bits_of(key_type);
+    uint64_t i;
+
+    if (w == 0 || begin_bit < 0 || end_bit > w || begin_bit > end_bit)
+        return ORACLE_BAD_ARGS;
+    passes = (end_bit - begin_bit + 7) / 8;
+    for (i = 0; i < (uint64_t)passes * 256u; ++i)
+        counts[i] = 0;
+    for (i = 0; i < n; ++i) {
+        uint64_t pat = order_pattern(key_type, descending, keys, i);
+        for (p = 0; p < passes; ++p) {
+            int shift = begin_bit + 8 * p;
+            int width = end_bit - shift;
+            if (width > 8)
+                width = 8;
+            counts[(uint64_t)p * 256u + digit_at64(pat, shift, width)] += 1;
+        }
+    }
+    return passes;
+}
+
+/*
+ * The multi-key exercise: stably sort by `first`, then stably sort that
+ * result by `second`.  Outputs the permuted first keys, second keys and
+ * (optional) values.
+ */
+int oracle_sort_two_keys(const uint32_t *first, const uint32_t *second, const uint32_t *vals,
+                         uint32_t *first_out, uint32_t *second_out, uint32_t *vals_out,
+                         uint64_t n)
+{
+    uint32_t *idx, *perm1, *tmp_keys, *second_by1, *perm;
+    uint64_t i;
+    int rc;
+
+    if ((vals == NULL) != (vals_out == NULL))
+        return ORACLE_BAD_ARGS;
+    if (n == 0)
+        return ORACLE_OK;
+    if (n > 0xFFFFFFFFu)
+        return ORACLE_BAD_ARGS;
+    idx = (uint32_t *)malloc(n * sizeof(uint32_t));
+    perm1 = (uint32_t *)malloc(n * sizeof(uint32_t));
+    tmp_keys = (uint32_t *)malloc(n * sizeof(uint32_t));
+    second_by1 = (uint32_t *)malloc(n * sizeof(uint32_t));
+    perm = (uint32_t *)malloc(n * sizeof(uint32_t));
+    if (!idx || !perm1 || !tmp_keys || !second_by1 || !perm) {
+        free(idx); free(perm1); free(tmp_keys); free(second_by1); free(perm);
+        return ORACLE_NO_MEMORY;
+    }
+    for (i = 0; i < n; ++i)
+        idx[i] = (uint32_t)i;
+    /* step 1: stable sort of the positions by the first key */
+    rc = oracle_lsd_sort_u32(first, idx, tmp_keys, perm1, n, 0, 32, 8);
+    if (rc == ORACLE_OK) {
+        /* step 2: stable sort of that order by the second key */
+        for (i = 0; i < n; ++i)
+            second_by1[i] = second[perm1[i]];
+        rc = oracle_lsd_sort_u32(second_by1, perm1, tmp_keys, perm, n, 0, 32, 8);
+    }
+    if (rc == ORACLE_OK) {
+        for (i = 0; i < n; ++i) {
+            first_out[i] = first[perm[i]];
+            second_out[i] = second[perm[i]];
+            if (vals)
+                vals_out[i] = vals[perm[i]];
+        }
+    }
+    free(idx); free(perm1); free(tmp_keys); free(second_by1); free(perm);
+    return rc;
 }

@@ -385,7 +385,219 @@ def pin_bitonic_tile(o, seed=9):
             assert np.array_equal(got[s:s + tile], seg[np.argsort(f, kind="stable")]), (n, tile, s)
 
 
+# --- key types, 64-bit keys, descending order, multi-key ---------------------------
+
+INT_TYPES = (np.uint32, np.int32, np.uint64, np.int64)
+FLOAT_TYPES = (np.float32, np.float64)
+
+# IEEE 754 totalOrder ladder of binary64 patterns, smallest first.
+F64_LADDER = [
+    0xFFF8000000000000,  # -qNaN
+    0xFFF0000000000000,  # -inf
+    0xC000000000000000,  # -2.0
+    0xBFF0000000000000,  # -1.0
+    0x8010000000000000,  # -min normal
+    0x8000000000000001,  # -min subnormal
+    0x8000000000000000,  # -0.0
+    0x0000000000000000,  # +0.0
+    0x0000000000000001,  # +min subnormal
+    0x0010000000000000,  # +min normal
+    0x3FF0000000000000,  # +1.0
+    0x4000000000000000,  # +2.0
+    0x7FF0000000000000,  # +inf
+    0x7FF8000000000000,  # +qNaN
+]
+
+
+def total_order_key_bits(bits, width):
+    """IEEE 754 totalOrder of a binary32/binary64 pattern as a sortable tuple."""
+    bits = int(bits)
+    sign = bits >> (width - 1)
+    mag = bits & ((1 << (width - 1)) - 1)
+    return (0, -mag) if sign else (1, mag)
+
+
+def typed_sample(rng, dtype, n):
+    """Keys of `dtype` with duplicates, extremes and (for floats) specials."""
+    if dtype in (np.uint32, np.int32):
+        raw = rng.integers(0, 2**32, n, dtype=np.uint32)
+        pool = np.array([0, 1, 0x7FFFFFFF, 0x80000000, 0x80000001, 0xFFFFFFFF, 0x12345678],
+                        np.uint32)
+        pick = rng.integers(0, 3, n) == 0
+        raw[pick] = pool[rng.integers(0, pool.size, int(pick.sum()))]
+        return raw.view(dtype)
+    if dtype == np.float32:
+        return random_float_patterns(rng, n).view(np.float32)
+    raw = rng.integers(0, 2**64, n, dtype=np.uint64)
+    if dtype == np.float64:
+        cls = rng.integers(0, 4, n)
+        ladder = np.array(F64_LADDER, np.uint64)
+        raw[cls == 1] = ladder[rng.integers(0, ladder.size, n)][cls == 1]
+        raw[cls == 2] = raw[cls == 2] & np.uint64(0x800FFFFFFFFFFFFF)   # subnormals, zeros
+        return raw.view(np.float64)
+    pool = np.array([0, 1, 0x7FFFFFFFFFFFFFFF, 0x8000000000000000, 0xFFFFFFFFFFFFFFFF,
+                     0x00000000FFFFFFFF, 0x0000000100000000, 0xFFFFFFFF00000000], np.uint64)
+    pick = rng.integers(0, 3, n) == 0
+    raw[pick] = pool[rng.integers(0, pool.size, int(pick.sum()))]
+    return raw.view(dtype)
+
+
+def value_key(x, dtype):
+    """Sort key from the value: Python ints, or totalOrder for floats."""
+    if dtype in INT_TYPES:
+        return int(x)
+    width = np.dtype(dtype).itemsize * 8
+    bits = np.array([x], dtype).view(np.uint32 if width == 32 else np.uint64)[0]
+    return total_order_key_bits(bits, width)
+
+
+def order_pattern_np(keys, descending=False):
+    """Order patterns of typed keys, written with numpy bit operations (an
+    XOR form of the offsets and transforms the oracle states arithmetically)."""
+    dt = keys.dtype.type
+    if dt in (np.uint32, np.int32, np.float32):
+        u = keys.view(np.uint32).copy()
+        top = np.uint32(0x80000000)
+        allb = np.uint32(0xFFFFFFFF)
+    else:
+        u = keys.view(np.uint64).copy()
+        top = np.uint64(1 << 63)
+        allb = np.uint64(0xFFFFFFFFFFFFFFFF)
+    if dt in (np.int32, np.int64):
+        u ^= top
+    elif dt in (np.float32, np.float64):
+        neg = (u & top) != 0
+        u = np.where(neg, u ^ allb, u | top)
+    if descending:
+        u ^= allb
+    return u
+
+
+def pin_typed_bruteforce(o, cases=240, seed=10):
+    """Full-range typed sorts against Python's stable sorted on the values."""
+    rng = np.random.default_rng(seed)
+    types = INT_TYPES + FLOAT_TYPES
+    for c in range(cases):
+        dt = types[c % len(types)]
+        desc = (c // len(types)) % 2 == 1
+        n = int(rng.integers(0, 97))
+        keys = typed_sample(rng, dt, n)
+        vals = np.arange(n, dtype=np.uint32)
+        ref = sorted(range(n), key=lambda i: value_key(keys[i], dt), reverse=desc)
+        k, v = o.sort_typed(keys, vals, descending=desc)
+        assert list(v) == ref, (dt, desc, c)
+        width = np.dtype(dt).itemsize * 8
+        raw = np.uint32 if width == 32 else np.uint64
+        assert np.array_equal(k.view(raw), keys.view(raw)[np.array(ref, np.int64)] if n else
+                              keys.view(raw)), (dt, desc, c)
+        assert np.array_equal(o.sort_typed(keys, None, descending=desc).view(raw), k.view(raw))
+        if dt in FLOAT_TYPES:
+            # non-NaN values by float comparison, -0.0 before +0.0 (reversed when descending)
+            fin = np.array([i for i in range(n) if not math.isnan(float(keys[i]))], np.int64)
+            sub = keys[fin] if fin.size else keys[:0]
+            key = lambda i: (float(sub[i]), math.copysign(1.0, float(sub[i])))
+            ref2 = sorted(range(sub.size), key=key, reverse=desc)
+            _, v2 = o.sort_typed(sub, np.arange(sub.size, dtype=np.uint32), descending=desc)
+            assert list(v2) == ref2, (dt, desc, c)
+
+
+def pin_typed_bit_ranges(o, n=1 << 14, seed=11):
+    """Partial bit ranges select bits of the order pattern: the permutation is
+    numpy's stable argsort of that field."""
+    rng = np.random.default_rng(seed)
+    for dt in INT_TYPES + FLOAT_TYPES:
+        width = np.dtype(dt).itemsize * 8
+        keys = typed_sample(rng, dt, n)
+        vals = np.arange(n, dtype=np.uint32)
+        for desc in (False, True):
+            pat = order_pattern_np(keys, desc).astype(np.uint64)
+            for _ in range(4):
+                b = int(rng.integers(0, width + 1))
+                e = int(rng.integers(b, width + 1))
+                mask = np.uint64((1 << (e - b)) - 1) if e - b < 64 else np.uint64(0xFFFFFFFFFFFFFFFF)
+                f = (pat >> np.uint64(b)) & mask
+                ref = np.argsort(f, kind="stable")
+                digit_bits = int(rng.choice([3, 8, 11]))
+                _, v = o.sort_typed(keys, vals, b, e, desc, digit_bits)
+                assert np.array_equal(v, ref.astype(np.uint32)), (dt, desc, b, e)
+
+
+def pin_u64_lsd(o, seed=12):
+    """64-bit LSD sort: exhaustive tiny arrays over an alphabet that differs in
+    both words, and numpy's stable argsort on random fields."""
+    alpha = [0x0000000000000000, 0x00000000FFFFFFFF, 0x0000000100000000, 0xFFFFFFFF00000001]
+    for n in range(0, 6):
+        for combo in itertools.product(alpha, repeat=n):
+            keys = np.array(combo, np.uint64)
+            vals = np.arange(n, dtype=np.uint32)
+            for (b, e) in [(0, 64), (0, 32), (32, 64), (28, 36), (31, 33), (5, 5)]:
+                ref = sorted(range(n), key=lambda i: (int(keys[i]) >> b) & ((1 << (e - b)) - 1))
+                k, v = o.sort_u64(keys, vals, b, e)
+                assert list(v) == ref, (combo, b, e)
+    rng = np.random.default_rng(seed)
+    n = 1 << 16
+    keys = rng.integers(0, 2**64, n, dtype=np.uint64)
+    keys[: n // 4] &= np.uint64(0xFFFF0000FFFF00FF)
+    vals = np.arange(n, dtype=np.uint32)
+    for (b, e, bits) in [(0, 64, 8), (0, 64, 16), (3, 61, 5), (30, 40, 8), (0, 33, 11)]:
+        f = (keys >> np.uint64(b)) & np.uint64((1 << (e - b)) - 1 if e - b < 64 else 2**64 - 1)
+        k, v = o.sort_u64(keys, vals, b, e, bits)
+        assert np.array_equal(v, np.argsort(f, kind="stable").astype(np.uint32)), (b, e, bits)
+        assert np.array_equal(k, keys[v])
+
+
+def pin_two_keys(o, seed=13):
+    """Multi-key: brute force on tiny inputs and numpy's lexsort (a stable
+    sort on the last key, then the one before) on larger ones."""
+    rng = np.random.default_rng(seed)
+    for c in range(150):
+        n = int(rng.integers(0, 40))
+        first = rng.integers(0, 4, n, dtype=np.uint32) * np.uint32(0x40000001)
+        second = rng.integers(0, 3, n, dtype=np.uint32) << np.uint32(30)
+        vals = np.arange(n, dtype=np.uint32)
+        ref = sorted(range(n), key=lambda i: (int(second[i]), int(first[i])))
+        f, s2, v = o.sort_two_keys(first, second, vals)
+        assert list(v) == ref, c
+        assert np.array_equal(f, first[v]) and np.array_equal(s2, second[v])
+    n = 1 << 16
+    first = rng.integers(0, 2**32, n, dtype=np.uint32)
+    first[: n // 2] &= np.uint32(0xF)
+    second = rng.integers(0, 50, n, dtype=np.uint32)
+    vals = np.arange(n, dtype=np.uint32)
+    f, s2, v = o.sort_two_keys(first, second, vals)
+    assert np.array_equal(v, np.lexsort((first, second)).astype(np.uint32))
+    f2, s3 = o.sort_two_keys(first, second)
+    assert np.array_equal(f2, f) and np.array_equal(s3, s2)
+
+
+def pin_histograms_typed(o, n=1 << 15, seed=14):
+    """Typed digit counts equal numpy's bincount of the order pattern's digits,
+    and the top-digit counts of signed keys equal a count by value ranges."""
+    rng = np.random.default_rng(seed)
+    for dt in INT_TYPES + FLOAT_TYPES:
+        width = np.dtype(dt).itemsize * 8
+        keys = typed_sample(rng, dt, n)
+        for desc in (False, True):
+            pat = order_pattern_np(keys, desc).astype(np.uint64)
+            for (b, e) in [(0, width), (4, width - 3), (width - 8, width)]:
+                h = o.digit_histograms_typed(keys, b, e, desc)
+                for p in range(h.shape[0]):
+                    s = b + 8 * p
+                    w = min(8, e - s)
+                    d = (pat >> np.uint64(s)) & np.uint64((1 << w) - 1)
+                    ref = np.bincount(d.astype(np.int64), minlength=256).astype(np.uint64)
+                    assert np.array_equal(h[p], ref), (dt, desc, b, e, p)
+    # signed keys: the top 8 bits of the pattern count the keys in the value
+    # ranges [-2^31 + k 2^24, -2^31 + (k + 1) 2^24)
+    x = rng.integers(-2**31, 2**31, n, dtype=np.int64).astype(np.int32)
+    h = o.digit_histograms_typed(x, 24, 32)
+    by_range = np.bincount(((x.astype(np.int64) + 2**31) // 2**24), minlength=256)
+    assert np.array_equal(h[0], by_range.astype(np.uint64))
+
+
 QUICK_PINS = [pin_radix_golden, pin_compaction_golden, pin_bitonic_golden,
               pin_bruteforce_exhaustive, pin_bruteforce_random, pin_float_order,
               pin_float_transform_sampled, pin_invariants_large, pin_digit_width_invariance,
-              pin_special_cases, pin_histograms, pin_compaction, pin_bitonic_tile]
+              pin_special_cases, pin_histograms, pin_compaction, pin_bitonic_tile,
+              pin_typed_bruteforce, pin_typed_bit_ranges, pin_u64_lsd, pin_two_keys,
+              pin_histograms_typed]

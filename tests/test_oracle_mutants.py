@@ -55,6 +55,44 @@ MUTANTS = [
      "width = 8;\n        for (i = 0; i < n; ++i) {"),
     ("bitonic tile sorts across tile boundaries",
      "uint64_t len = (n - s < tile) ? (n - s) : tile;", "uint64_t len = n - s;"),
+    ("signed 32-bit keys not offset",
+     "p = (uint64_t)((int64_t)((const int32_t *)keys)[i] + ((int64_t)1 << 31));",
+     "p = (uint32_t)((const int32_t *)keys)[i];"),
+    ("signed 64-bit keys not offset",
+     "p = ((const uint64_t *)keys)[i] + ((uint64_t)1 << 63);", "p = ((const uint64_t *)keys)[i];"),
+    ("negative doubles not inverted",
+     "p = (p & top) ? ~p : (p | top);", "p = (p & top) ? p : (p | top);"),
+    ("descending order not complemented",
+     "p = all - p;", "p = p + 0 * all;"),
+    ("descending complement of 64-bit keys on 32 bits",
+     "uint64_t all = (w == 64) ? ~(uint64_t)0 : (uint64_t)0xFFFFFFFFu;",
+     "uint64_t all = (uint64_t)0xFFFFFFFFu;"),
+    ("64-bit sort skips the digits of the high word",
+     "        counting_sort_pass64(ka, va, kb, vb, n, shift, width, cnt);",
+     "        if (shift >= 32)\n            continue;\n        counting_sort_pass64(ka, va, kb, vb, n, shift, width, cnt);"),
+    ("64-bit digit taken from the low word only",
+     "return (key >> shift) & low_bits;", "return ((uint32_t)key >> (shift & 31)) & low_bits;"),
+    ("64-bit sort: last digit not narrowed",
+     "int width = (end_bit - shift < digit_bits) ? end_bit - shift : digit_bits;",
+     "int width = digit_bits;"),
+    ("64-bit sort: pass loop stops one digit early",
+     "for (shift = begin_bit; end_bit > shift; shift += digit_bits)",
+     "for (shift = begin_bit; end_bit > shift + digit_bits; shift += digit_bits)"),
+    ("64-bit pass: inclusive scan",
+     "cnt[d] = running;\n        running += here;", "running += here;\n        cnt[d] = running;"),
+    ("64-bit pass: values not moved with their keys",
+     "dst_vals[at] = src_vals[j];", "dst_vals[at] = src_vals[at];"),
+    ("64-bit pass: scatter in reverse input order",
+     "for (j = 0; j < n; ++j) {\n        uint64_t dg", "for (j = n; j-- > 0;) {\n        uint64_t dg"),
+    ("two-key sort: first step sorts by the second key",
+     "rc = oracle_lsd_sort_u32(first, idx, tmp_keys, perm1, n, 0, 32, 8);",
+     "rc = oracle_lsd_sort_u32(second, idx, tmp_keys, perm1, n, 0, 32, 8);"),
+    ("two-key sort: second step forgets the first step's order",
+     "rc = oracle_lsd_sort_u32(second_by1, perm1, tmp_keys, perm, n, 0, 32, 8);",
+     "rc = oracle_lsd_sort_u32(second, idx, tmp_keys, perm, n, 0, 32, 8);"),
+    ("typed histogram ignores descending order",
+     "uint64_t pat = order_pattern(key_type, descending, keys, i);",
+     "uint64_t pat = order_pattern(key_type, 0, keys, i);"),
 ]
 
 
