@@ -72,16 +72,30 @@ __device__ __forceinline__ uint32_t next_chunked_tile(uint32_t* sched, uint32_t 
     return t < tiles ? static_cast<uint32_t>(t) : tiles;
 }
 
-// Order-preserving transform of binary32 patterns: flips every bit of a
-// negative pattern and only the sign bit of a non-negative one.
-__device__ __forceinline__ uint32_t float_to_sortable(uint32_t u) {
-    uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31) | 0x80000000u;
-    return u ^ m;
+// Order transform of a sort's keys.  Every key type and direction maps a key
+// to an unsigned pattern whose unsigned order is the wanted order by XOR-ing
+// each 32-bit word with a mask chosen by the key's sign bit (the top bit of
+// the word `hi`, which holds it; a 32-bit key is a lone `hi` word):
+//   u32/u64  ascending: 0                 descending: all ones
+//   i32/i64  ascending: sign bit flipped  descending: the other bits flipped
+//   f32/f64  ascending: negative keys all bits flipped, others the sign bit;
+//            descending: the complement of that.
+// The inverse has the same form with the masks of the two signs swapped
+// when the masks flip the sign bit.
+struct KeyXform {
+    uint32_t pos_hi, neg_hi;   // masks of the word holding the sign bit
+    uint32_t pos_lo, neg_lo;   // masks of the low word of a 64-bit key
+};
+
+__device__ __forceinline__ uint32_t xform32(uint32_t u, const KeyXform& x) {
+    return u ^ ((static_cast<int32_t>(u) < 0) ? x.neg_hi : x.pos_hi);
 }
 
-__device__ __forceinline__ uint32_t sortable_to_float(uint32_t s) {
-    uint32_t m = static_cast<uint32_t>(static_cast<int32_t>(~s) >> 31) | 0x80000000u;
-    return s ^ m;
+__device__ __forceinline__ uint64_t xform64(uint64_t k, const KeyXform& x) {
+    const bool neg = static_cast<int64_t>(k) < 0;
+    const uint32_t mh = neg ? x.neg_hi : x.pos_hi;
+    const uint32_t ml = neg ? x.neg_lo : x.pos_lo;
+    return k ^ ((static_cast<uint64_t>(mh) << 32) | ml);
 }
 
 // Inclusive sum over the 64 lanes of a wave.
