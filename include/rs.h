@@ -6,6 +6,10 @@
  *   rs_sort_pairs_u32       stable sort of 32-bit keys with 32-bit values
  *   rs_sort_pairs_f32       stable sort of float keys (IEEE 754 total order)
  *                           with 32-bit values
+ *   rs_sort_keys            stable sort of u32/i32/f32/u64/i64/f64 keys,
+ *   rs_sort_pairs           ascending or descending, with or without values
+ *   rs_sort_two_keys_u32    stable sort by (major, minor) u32 key pairs
+ *   rs_digit_counts         every 8-bit pass's digit counts of typed keys
  *   rs_compact_positive_f32 keep x > 0 in order, zero-fill the rest, count
  *   rs_bitonic_tile         sort each run of at most 1024 keys in LDS
  *   rs_status_string        text of a status code
@@ -34,7 +38,9 @@
  *    per process from the device current at the first call; a grid only
  *    affects speed, never results.
  *  - n < 2^30 (RS_ERR_UNSUPPORTED_SIZE otherwise): cross-tile prefix states
- *    hold 30-bit counts beside 2 status bits.
+ *    hold 30-bit counts beside 2 status bits.  Sorts of 64-bit keys and
+ *    two-key sorts take n < 2^29, which keeps every byte offset into an
+ *    array of 8-byte keys below 2^32.
  *  - Scheduling assumption of the persistent kernels (sort passes and
  *    compaction): their grid never exceeds the number of blocks that fit on
  *    the device at once, tiles are handed out in increasing order per group
@@ -59,7 +65,7 @@ extern "C" {
 typedef enum rs_status {
     RS_OK = 0,
     RS_ERR_INVALID_VALUE = 1,    /* null pointer with n > 0, bad bit range, bad tile */
-    RS_ERR_UNSUPPORTED_SIZE = 2, /* n >= 2^30 */
+    RS_ERR_UNSUPPORTED_SIZE = 2, /* n >= 2^30 (2^29 for 8-byte and two-key sorts) */
     RS_ERR_TEMP_TOO_SMALL = 3,   /* *temp_bytes below the queried size */
     RS_ERR_OVERLAP = 4,          /* two of the buffers overlap */
     RS_ERR_MISALIGNED = 5,       /* a pointer is not 16-byte aligned */
@@ -67,6 +73,29 @@ typedef enum rs_status {
 } rs_status;
 
 #define RS_MAX_N ((uint64_t)1 << 30)
+#define RS_MAX_N64 ((uint64_t)1 << 29)
+
+/*
+ * Key types of rs_sort_keys / rs_sort_pairs / rs_digit_counts.  Keys are
+ * arrays of 4-byte (u32, i32, f32) or 8-byte (u64, i64, f64) elements.
+ * Each key maps to an unsigned order pattern of the same width whose
+ * unsigned order is the type's order: unsigned keys as they are, signed keys
+ * with the sign bit flipped (value + 2^(w-1)), floats with every bit of a
+ * negative pattern flipped and the sign bit of any other set, which is IEEE
+ * 754 totalOrder (-NaN < -inf < ... < -0.0 < +0.0 < ... < +inf < +NaN,
+ * subnormals kept); a descending sort uses the complement of the pattern
+ * ("第10章 并行模式：排序 - GPU上的排序", 八、习题: the exercises on
+ * descending sorts, float preprocessing and 64-bit keys).  Equal keys keep
+ * their input order in both directions.
+ */
+typedef enum rs_key_type {
+    RS_KEY_U32 = 0,
+    RS_KEY_I32 = 1,
+    RS_KEY_F32 = 2,
+    RS_KEY_U64 = 3,
+    RS_KEY_I64 = 4,
+    RS_KEY_F64 = 5
+} rs_key_type;
 
 /*
  * Stable LSD radix sort of keys by bits [begin_bit, end_bit).
@@ -116,6 +145,61 @@ rs_status rs_sort_pairs_f32(const float *keys_in, float *keys_out,
                             const uint32_t *vals_in, uint32_t *vals_out, uint64_t n,
                             int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
                             hipStream_t stream);
+
+/*
+ * Stable LSD radix sort of typed keys (see rs_key_type), ascending or (with
+ * descending != 0) descending, by bits [begin_bit, end_bit) of the keys'
+ * order patterns, 0 <= begin_bit <= end_bit <= 32 (4-byte keys) or 64
+ * (8-byte keys); (0, 32) or (0, 64) is the full order.  With 8-bit digits a
+ * 64-bit key takes eight passes ("第10章 并行模式：排序", 八、习题, the
+ * iteration-count exercise).  keys_in [n] read only, keys_out [n] written
+ * (the original bit patterns in sorted order).  n < 2^30 for 4-byte keys,
+ * n < 2^29 for 8-byte keys.  Temp, streams and errors as for
+ * rs_sort_keys_u32 (RS_ERR_INVALID_VALUE also for an unknown key type).
+ * Up to 16384 4-byte keys the sort runs in one workgroup; 8-byte keys always
+ * take the digit-count launch and one launch per pass.
+ */
+rs_status rs_sort_keys(rs_key_type key_type, int descending, const void *keys_in, void *keys_out,
+                       uint64_t n, int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
+                       hipStream_t stream);
+
+/*
+ * As rs_sort_keys, with u32 values that move with their keys (vals_in [n]
+ * read only, vals_out [n] written).
+ */
+rs_status rs_sort_pairs(rs_key_type key_type, int descending, const void *keys_in, void *keys_out,
+                        const uint32_t *vals_in, uint32_t *vals_out, uint64_t n, int begin_bit,
+                        int end_bit, void *d_temp, size_t *temp_bytes, hipStream_t stream);
+
+/*
+ * Multi-key sort ("第10章 并行模式：排序", 八、习题, the exercise on sorting
+ * by one key and then stably by another): orders n elements by major key,
+ * then by minor key, then by input position.  It is one stable LSD sort of
+ * the 64-bit key major * 2^32 + minor, read from and written back to two
+ * u32 arrays (the passes in between keep 8-byte keys in temp).  The result
+ * equals a stable sort by the minor key followed by a stable sort by the
+ * major key.  major_in/minor_in [n] read only, major_out/minor_out [n]
+ * written; vals_in/vals_out [n] u32, or both NULL for keys only.  n < 2^29.
+ * Temp, streams and errors as for rs_sort_keys_u32.
+ */
+rs_status rs_sort_two_keys_u32(const uint32_t *major_in, const uint32_t *minor_in,
+                               uint32_t *major_out, uint32_t *minor_out, const uint32_t *vals_in,
+                               uint32_t *vals_out, uint64_t n, void *d_temp, size_t *temp_bytes,
+                               hipStream_t stream);
+
+/*
+ * Digit counts of every 8-bit pass over bits [begin_bit, end_bit) of the
+ * order patterns of typed keys, in one read of the keys (the first kernel of
+ * the multi-bit radix sort, "CUDA 算子笔记 3", section 一次处理多位):
+ * d_counts[p * 256 + d] = number of keys whose pass-p digit is d, pass p
+ * covering bits [begin_bit + 8p, min(begin_bit + 8p + 8, end_bit)).
+ * d_counts: ceil((end_bit - begin_bit) / 8) * 256 u32 in device memory,
+ * 4-byte aligned, overwritten (zeros when n == 0; untouched when
+ * begin_bit == end_bit).  keys [n], 16-byte aligned, read only.  These are
+ * the counts every sort call computes first.  Errors as for rs_sort_keys.
+ */
+rs_status rs_digit_counts(rs_key_type key_type, int descending, const void *keys, uint64_t n,
+                          int begin_bit, int end_bit, uint32_t *d_counts, hipStream_t stream);
 
 /*
  * Stream compaction: out[0..k) = the inputs with x > 0.0f in input order,

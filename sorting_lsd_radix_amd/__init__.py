@@ -19,9 +19,12 @@ import os
 __all__ = [
     "RsError", "RS_OK", "RS_ERR_INVALID_VALUE", "RS_ERR_UNSUPPORTED_SIZE",
     "RS_ERR_TEMP_TOO_SMALL", "RS_ERR_OVERLAP", "RS_ERR_MISALIGNED", "RS_ERR_HIP",
-    "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_compact_positive_f32",
+    "RS_KEY_U32", "RS_KEY_I32", "RS_KEY_F32", "RS_KEY_U64", "RS_KEY_I64", "RS_KEY_F64",
+    "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_sort_keys", "rs_sort_pairs",
+    "rs_sort_two_keys_u32", "rs_digit_counts", "rs_compact_positive_f32",
     "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
-    "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "compact_positive_f32", "bitonic_tile",
+    "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "sort_keys", "sort_pairs",
+    "sort_two_keys_u32", "digit_counts", "compact_positive_f32", "bitonic_tile",
     "library_path", "use_library", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
 ]
 
@@ -36,6 +39,13 @@ RS_ERR_OVERLAP = 4
 RS_ERR_MISALIGNED = 5
 RS_ERR_HIP = 6
 
+RS_KEY_U32 = 0
+RS_KEY_I32 = 1
+RS_KEY_F32 = 2
+RS_KEY_U64 = 3
+RS_KEY_I64 = 4
+RS_KEY_F64 = 5
+
 RS_KERNEL_UPSWEEP = 0
 RS_KERNEL_ONESWEEP = 1
 RS_KERNEL_SORT_INIT = 2
@@ -48,6 +58,7 @@ KERNEL_NAMES = {0: "upsweep", 1: "onesweep", 2: "sort_init", 3: "compact_init",
                 4: "compact", 5: "bitonic", 6: "copy", 7: "tile_sort"}
 
 EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32",
+                    "rs_sort_keys", "rs_sort_pairs", "rs_sort_two_keys_u32", "rs_digit_counts",
                     "rs_compact_positive_f32", "rs_bitonic_tile", "rs_status_string",
                     "rs_timing_enable", "rs_timing_collect"]
 
@@ -89,9 +100,14 @@ def _load():
     lib.rs_sort_keys_u32.argtypes = [vp, vp, u64, i32, i32, vp, szp, vp]
     lib.rs_sort_pairs_u32.argtypes = [vp, vp, vp, vp, u64, i32, i32, vp, szp, vp]
     lib.rs_sort_pairs_f32.argtypes = [vp, vp, vp, vp, u64, i32, i32, vp, szp, vp]
+    lib.rs_sort_keys.argtypes = [i32, i32, vp, vp, u64, i32, i32, vp, szp, vp]
+    lib.rs_sort_pairs.argtypes = [i32, i32, vp, vp, vp, vp, u64, i32, i32, vp, szp, vp]
+    lib.rs_sort_two_keys_u32.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp, szp, vp]
+    lib.rs_digit_counts.argtypes = [i32, i32, vp, u64, i32, i32, vp, vp]
     lib.rs_compact_positive_f32.argtypes = [vp, vp, vp, u64, vp, szp, vp]
     lib.rs_bitonic_tile.argtypes = [vp, vp, u64, u32, i32, i32, vp]
-    for f in (lib.rs_sort_keys_u32, lib.rs_sort_pairs_u32, lib.rs_sort_pairs_f32,
+    for f in (lib.rs_sort_keys_u32, lib.rs_sort_pairs_u32, lib.rs_sort_pairs_f32, lib.rs_sort_keys,
+              lib.rs_sort_pairs, lib.rs_sort_two_keys_u32, lib.rs_digit_counts,
               lib.rs_compact_positive_f32, lib.rs_bitonic_tile):
         f.restype = i32
     lib.rs_status_string.argtypes = [i32]
@@ -162,6 +178,48 @@ def rs_sort_pairs_f32(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bi
     return _sort_call(_load().rs_sort_pairs_f32, "rs_sort_pairs_f32",
                       (keys_in, keys_out, vals_in, vals_out), n, begin_bit, end_bit, d_temp,
                       temp_bytes, stream)
+
+
+def rs_sort_keys(key_type, descending, keys_in, keys_out, n, begin_bit, end_bit, d_temp,
+                 temp_bytes, stream=None):
+    """C: rs_sort_keys.  With d_temp None, returns the temp size."""
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = _load().rs_sort_keys(int(key_type), int(bool(descending)), _ptr(keys_in), _ptr(keys_out),
+                              int(n), int(begin_bit), int(end_bit), _ptr(d_temp),
+                              ctypes.byref(size), _stream(stream) if d_temp is not None else None)
+    _call("rs_sort_keys", st)
+    return size.value if d_temp is None else None
+
+
+def rs_sort_pairs(key_type, descending, keys_in, keys_out, vals_in, vals_out, n, begin_bit,
+                  end_bit, d_temp, temp_bytes, stream=None):
+    """C: rs_sort_pairs.  With d_temp None, returns the temp size."""
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = _load().rs_sort_pairs(int(key_type), int(bool(descending)), _ptr(keys_in), _ptr(keys_out),
+                               _ptr(vals_in), _ptr(vals_out), int(n), int(begin_bit), int(end_bit),
+                               _ptr(d_temp), ctypes.byref(size),
+                               _stream(stream) if d_temp is not None else None)
+    _call("rs_sort_pairs", st)
+    return size.value if d_temp is None else None
+
+
+def rs_sort_two_keys_u32(major_in, minor_in, major_out, minor_out, vals_in, vals_out, n, d_temp,
+                         temp_bytes, stream=None):
+    """C: rs_sort_two_keys_u32.  With d_temp None, returns the temp size."""
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = _load().rs_sort_two_keys_u32(_ptr(major_in), _ptr(minor_in), _ptr(major_out),
+                                      _ptr(minor_out), _ptr(vals_in), _ptr(vals_out), int(n),
+                                      _ptr(d_temp), ctypes.byref(size),
+                                      _stream(stream) if d_temp is not None else None)
+    _call("rs_sort_two_keys_u32", st)
+    return size.value if d_temp is None else None
+
+
+def rs_digit_counts(key_type, descending, keys, n, begin_bit, end_bit, d_counts, stream=None):
+    """C: rs_digit_counts."""
+    st = _load().rs_digit_counts(int(key_type), int(bool(descending)), _ptr(keys), int(n),
+                                 int(begin_bit), int(end_bit), _ptr(d_counts), _stream(stream))
+    _call("rs_digit_counts", st)
 
 
 def rs_compact_positive_f32(x_in, x_out, d_count, n, d_temp, temp_bytes, stream=None):
@@ -253,6 +311,73 @@ def sort_pairs_f32(keys, vals, begin_bit=0, end_bit=32, keys_out=None, vals_out=
     rs_sort_pairs_f32(keys, keys_out, vals, vals_out, n, begin_bit, end_bit, temp, temp.numel(),
                       stream)
     return keys_out, vals_out
+
+
+def _key_type(t):
+    import torch
+    table = {torch.uint32: RS_KEY_U32, torch.int32: RS_KEY_I32, torch.float32: RS_KEY_F32,
+             torch.uint64: RS_KEY_U64, torch.int64: RS_KEY_I64, torch.float64: RS_KEY_F64}
+    if not t.is_cuda or not t.is_contiguous() or t.dtype not in table:
+        raise TypeError("keys must be a contiguous CUDA tensor of uint32, int32, float32, "
+                        "uint64, int64 or float64")
+    return table[t.dtype], t.element_size() * 8
+
+
+def sort_keys(keys, descending=False, begin_bit=0, end_bit=None, out=None, temp=None, stream=None):
+    """Stable sort of a typed key tensor (ascending or descending); returns the sorted keys."""
+    kt, width = _key_type(keys)
+    end_bit = width if end_bit is None else end_bit
+    n = keys.numel()
+    out = keys.new_empty(keys.shape) if out is None else out
+    need = rs_sort_keys(kt, descending, None, None, n, begin_bit, end_bit, None, 0)
+    temp = _temp(need, keys.device) if temp is None else temp
+    rs_sort_keys(kt, descending, keys, out, n, begin_bit, end_bit, temp, temp.numel(), stream)
+    return out
+
+
+def sort_pairs(keys, vals, descending=False, begin_bit=0, end_bit=None, keys_out=None,
+               vals_out=None, temp=None, stream=None):
+    """Stable sort of typed keys with uint32 values; returns (keys_out, vals_out)."""
+    import torch
+    kt, width = _key_type(keys)
+    _check_tensor(vals, torch.uint32, "vals")
+    end_bit = width if end_bit is None else end_bit
+    n = keys.numel()
+    keys_out = keys.new_empty(keys.shape) if keys_out is None else keys_out
+    vals_out = torch.empty_like(vals) if vals_out is None else vals_out
+    need = rs_sort_pairs(kt, descending, None, None, None, None, n, begin_bit, end_bit, None, 0)
+    temp = _temp(need, keys.device) if temp is None else temp
+    rs_sort_pairs(kt, descending, keys, keys_out, vals, vals_out, n, begin_bit, end_bit, temp,
+                  temp.numel(), stream)
+    return keys_out, vals_out
+
+
+def sort_two_keys_u32(major, minor, vals=None, temp=None, stream=None):
+    """Stable sort by (major, minor) uint32 keys; returns (major, minor) or (major, minor, vals)."""
+    import torch
+    _check_tensor(major, torch.uint32, "major")
+    _check_tensor(minor, torch.uint32, "minor")
+    n = major.numel()
+    mo, no = torch.empty_like(major), torch.empty_like(minor)
+    vo = None
+    if vals is not None:
+        _check_tensor(vals, torch.uint32, "vals")
+        vo = torch.empty_like(vals)
+    need = rs_sort_two_keys_u32(None, None, None, None, None, None, n, None, 0)
+    temp = _temp(need, major.device) if temp is None else temp
+    rs_sort_two_keys_u32(major, minor, mo, no, vals, vo, n, temp, temp.numel(), stream)
+    return (mo, no) if vals is None else (mo, no, vo)
+
+
+def digit_counts(keys, descending=False, begin_bit=0, end_bit=None, stream=None):
+    """Per-pass 8-bit digit counts of a typed key tensor: uint32 tensor [passes, 256]."""
+    import torch
+    kt, width = _key_type(keys)
+    end_bit = width if end_bit is None else end_bit
+    passes = (end_bit - begin_bit + 7) // 8
+    counts = torch.zeros((max(passes, 1), 256), dtype=torch.uint32, device=keys.device)
+    rs_digit_counts(kt, descending, keys, keys.numel(), begin_bit, end_bit, counts, stream)
+    return counts[:passes]
 
 
 def compact_positive_f32(x, out=None, count=None, temp=None, stream=None):

@@ -5,6 +5,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "internal.hpp"   // KeyXform
+
 namespace rs {
 
 constexpr int kWave = 64;          // CDNA wavefront width
@@ -81,14 +83,13 @@ __device__ __forceinline__ uint32_t next_chunked_tile(uint32_t* sched, uint32_t 
 //   f32/f64  ascending: negative keys all bits flipped, others the sign bit;
 //            descending: the complement of that.
 // The inverse has the same form with the masks of the two signs swapped
-// when the masks flip the sign bit.
-struct KeyXform {
-    uint32_t pos_hi, neg_hi;   // masks of the word holding the sign bit
-    uint32_t pos_lo, neg_lo;   // masks of the low word of a 64-bit key
-};
-
+// when the masks flip the sign bit.  (KeyXform is declared in internal.hpp.)
+// Written as u ^ pos ^ (sign & (pos ^ neg)) so that each instruction reads at
+// most one of the (uniform) masks: a CDNA vector instruction reads at most
+// one scalar register.
 __device__ __forceinline__ uint32_t xform32(uint32_t u, const KeyXform& x) {
-    return u ^ ((static_cast<int32_t>(u) < 0) ? x.neg_hi : x.pos_hi);
+    const uint32_t sign = static_cast<uint32_t>(static_cast<int32_t>(u) >> 31);
+    return (u ^ x.pos_hi) ^ (sign & (x.pos_hi ^ x.neg_hi));
 }
 
 __device__ __forceinline__ uint64_t xform64(uint64_t k, const KeyXform& x) {

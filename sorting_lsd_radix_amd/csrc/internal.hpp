@@ -28,13 +28,46 @@ TileGrid tile_grid(uint32_t tiles, uint32_t resident);
 
 // ---- radix sort ---------------------------------------------------------------
 
-// Temp bytes for a sort of n keys with `passes` 8-bit passes.
-size_t sort_temp_bytes(uint64_t n, bool pairs, int passes);
+// Order transform of a sort's keys: each 32-bit word of a key is XOR-ed with
+// pos_* when the key's sign bit (top bit of the word `hi`; a 32-bit key is a
+// lone `hi` word) is clear and with neg_* when it is set.
+struct KeyXform {
+    uint32_t pos_hi, neg_hi;   // masks of the word holding the sign bit
+    uint32_t pos_lo, neg_lo;   // masks of the low word of a 64-bit key
+};
 
-// Enqueues the whole sort (passes >= 1).  Arguments are already validated.
-hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32_t* vals_in,
-                       uint32_t* vals_out, uint32_t n, int begin_bit, int end_bit, bool is_f32,
+// What kind of keys a sort moves.
+struct SortKind {
+    bool key64;        // 8-byte keys (two words, low first)
+    bool soa;          // two-key sort: low words and high words in two arrays
+    bool transforms;   // xf is not the identity
+    KeyXform xf;       // forward order transform
+};
+
+// Buffers of a sort (device pointers).  keys_in/keys_out hold n u32 keys, n
+// 8-byte keys, or (soa) the n low words; hi_in/hi_out the n high words of a
+// two-key sort.  vals_* are null for keys only.
+struct SortIo {
+    const uint32_t* keys_in;
+    uint32_t* keys_out;
+    const uint32_t* hi_in;
+    uint32_t* hi_out;
+    const uint32_t* vals_in;
+    uint32_t* vals_out;
+    uint32_t n;
+};
+
+// Temp bytes for a sort of n keys (depends only on n, pairs and the kind).
+size_t sort_temp_bytes(uint64_t n, bool pairs, const SortKind& kind);
+
+// Enqueues the whole sort (begin_bit < end_bit).  Arguments are already validated.
+hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, int end_bit,
                        void* temp, hipStream_t stream);
+
+// Zeroes d_counts[passes][256] and adds every pass's digit counts of the
+// (transformed) keys of io into it.
+hipError_t launch_digit_counts(const SortIo& io, const SortKind& kind, int begin_bit, int end_bit,
+                               uint32_t* d_counts, hipStream_t stream);
 
 // Zeroes `words` u32 starting at p (a fill kernel; no memset nodes).
 hipError_t launch_fill_zero(uint32_t* p, uint64_t words, hipStream_t stream, int kernel_id);

@@ -1,5 +1,5 @@
-// radix.hip -- stable LSD radix sort of 32-bit keys (and key-value pairs) for
-// gfx950, one-sweep style with 8-bit digits.
+// radix.hip -- stable LSD radix sort of 32- and 64-bit keys (and key-value
+// pairs) for gfx950, one-sweep style with 8-bit digits.
 //
 // The method ("CUDA 算子笔记 3", section 一次处理多位): one read of the keys
 // counts the digits of every pass (upsweep); then each pass places every key
@@ -26,7 +26,17 @@
 //    is written to HBM with consecutive addresses;
 //  * tile ids come from an atomic counter, so a tile only ever waits on
 //    tiles that are already running; state words are read and written at
-//    agent scope because tiles on different XCDs sit behind different L2s.
+//    agent scope because tiles on different XCDs sit behind different L2s;
+//  * every key type and direction is a sign-dependent XOR of the key's words
+//    (KeyXform), applied on the first pass's load and undone on the last
+//    pass's store; the passes in between move the transformed patterns
+//    ("第10章 并行模式：排序", 八、习题: the float, descending and 64-bit
+//    exercises);
+//  * 64-bit keys take the same pass kernel with two words per key (8-byte
+//    loads, LDS slots and stores); a two-key sort reads the major and minor
+//    keys from two arrays in its first pass and writes them back to two
+//    arrays in its last, with 64-bit keys in between (the multi-key exercise:
+//    a stable LSD over the concatenated key).
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -80,7 +90,13 @@ constexpr int kUpBlock = 1024;   // many waves per CU hide the LDS atomics' late
 // their digits (128 KB for four passes: one block per CU).  8 sub-histograms
 // (bank = lane mod 8 and two digit bits) took 14 % longer at 2^28 keys.
 constexpr int kUpSub = 32;
-constexpr int kMaxPasses = 4;
+constexpr int kMaxPasses = 4;        // 8-bit passes of a 32-bit key
+constexpr int kMaxPasses64 = 8;      // ... of a 64-bit key
+// 64-bit keys: eight passes' counts with 16 sub-histograms per digit (128 KB).
+constexpr int kUpSub64 = 16;
+// 64-bit keys: 1024 x 16 tiles (16384 keys, 128 KB of 8-byte LDS slots).
+constexpr int kKey64Block = 1024;
+constexpr int kKey64Items = 16;
 
 constexpr size_t kAlign = 256;
 
@@ -106,16 +122,17 @@ __global__ __launch_bounds__(256) void fill_zero_kernel(uint32_t* __restrict__ p
 // on shared-memory histograms and spreading atomic contention.)
 // ---------------------------------------------------------------------------
 struct PassDigits {
-    uint32_t shift[kMaxPasses];
-    uint32_t mask[kMaxPasses];
-    uint32_t width[kMaxPasses];
+    uint32_t shift[kMaxPasses64];
+    uint32_t mask[kMaxPasses64];
+    uint32_t width[kMaxPasses64];
     uint32_t passes;
+    KeyXform xf;   // applied to each key before its digits are counted (XF kernels)
 };
 
-template <bool FLIP>
+template <bool XF>
 __device__ __forceinline__ void count_key(uint32_t* s_hist, uint32_t key, const PassDigits& pd,
                                           uint32_t sub) {
-    if (FLIP) key = float_to_sortable(key);
+    if (XF) key = xform32(key, pd.xf);
 #pragma unroll
     for (int p = 0; p < kMaxPasses; ++p) {
         if (p < static_cast<int>(pd.passes)) {
@@ -125,7 +142,7 @@ __device__ __forceinline__ void count_key(uint32_t* s_hist, uint32_t key, const 
     }
 }
 
-template <bool FLIP>
+template <bool XF>
 __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __restrict__ keys,
                                                            uint32_t n, PassDigits pd,
                                                            uint32_t* __restrict__ bins) {
@@ -149,21 +166,21 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
         for (int u = 0; u < 4; ++u) q[u] = __builtin_nontemporal_load(&k4[i + u * kUpBlock]);
 #pragma unroll
         for (int u = 0; u < 4; ++u) {
-            count_key<FLIP>(s_hist, q[u].x, pd, sub);
-            count_key<FLIP>(s_hist, q[u].y, pd, sub);
-            count_key<FLIP>(s_hist, q[u].z, pd, sub);
-            count_key<FLIP>(s_hist, q[u].w, pd, sub);
+            count_key<XF>(s_hist, q[u].x, pd, sub);
+            count_key<XF>(s_hist, q[u].y, pd, sub);
+            count_key<XF>(s_hist, q[u].z, pd, sub);
+            count_key<XF>(s_hist, q[u].w, pd, sub);
         }
     }
     for (; i < end; i += kUpBlock) {
         const u32x4 q = __builtin_nontemporal_load(&k4[i]);
-        count_key<FLIP>(s_hist, q.x, pd, sub);
-        count_key<FLIP>(s_hist, q.y, pd, sub);
-        count_key<FLIP>(s_hist, q.z, pd, sub);
-        count_key<FLIP>(s_hist, q.w, pd, sub);
+        count_key<XF>(s_hist, q.x, pd, sub);
+        count_key<XF>(s_hist, q.y, pd, sub);
+        count_key<XF>(s_hist, q.z, pd, sub);
+        count_key<XF>(s_hist, q.w, pd, sub);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * 4)
-        count_key<FLIP>(s_hist, keys[nvec * 4 + threadIdx.x], pd, sub);
+        count_key<XF>(s_hist, keys[nvec * 4 + threadIdx.x], pd, sub);
     __syncthreads();
 
     // Thread i sums bin i's sub-histograms starting at sub i mod 32, so the
@@ -172,6 +189,69 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
         uint32_t c = 0;
 #pragma unroll
         for (int s = 0; s < kUpSub; ++s) c += s_hist[i * kUpSub + ((i + s) % kUpSub)];
+        if (c) fetch_add_agent(&bins[i], c);
+    }
+}
+
+// Upsweep of 64-bit keys: up to eight passes' counts in one read.  The keys
+// are one array of 8-byte keys, or (SOA) a low-word and a high-word array.
+template <bool XF>
+__device__ __forceinline__ void count_key64(uint32_t* s_hist, uint64_t key, const PassDigits& pd,
+                                            uint32_t sub) {
+    if (XF) key = xform64(key, pd.xf);
+#pragma unroll
+    for (int p = 0; p < kMaxPasses64; ++p) {
+        if (p < static_cast<int>(pd.passes)) {
+            const uint32_t d = static_cast<uint32_t>(key >> pd.shift[p]) & pd.mask[p];
+            atomicAdd(&s_hist[(p * kRadix + d) * kUpSub64 + sub], 1u);
+        }
+    }
+}
+
+template <bool XF, bool SOA>
+__global__ __launch_bounds__(kUpBlock) void upsweep64_kernel(const uint32_t* __restrict__ keys,
+                                                             const uint32_t* __restrict__ keys_hi,
+                                                             uint32_t n, PassDigits pd,
+                                                             uint32_t* __restrict__ bins) {
+    __shared__ uint32_t s_hist[kMaxPasses64 * kRadix * kUpSub64];
+    for (int i = threadIdx.x; i < kMaxPasses64 * kRadix * kUpSub64; i += kUpBlock) s_hist[i] = 0u;
+    __syncthreads();
+
+    // one contiguous chunk of 16-byte vectors per block: two 8-byte keys per
+    // vector, or four low words and four high words
+    constexpr uint32_t PER_VEC = SOA ? 4u : 2u;
+    const uint32_t sub = threadIdx.x % kUpSub64;
+    const uint32_t nvec = n / PER_VEC;
+    const uint32_t per_block = (nvec + gridDim.x - 1) / gridDim.x;
+    const uint32_t begin = blockIdx.x * per_block;
+    const uint32_t end = (begin + per_block < nvec) ? begin + per_block : nvec;
+    const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
+    const u32x4* h4 = reinterpret_cast<const u32x4*>(keys_hi);
+    for (uint32_t i = begin + threadIdx.x; i < end; i += kUpBlock) {
+        const u32x4 q = __builtin_nontemporal_load(&k4[i]);
+        if (SOA) {
+            const u32x4 h = __builtin_nontemporal_load(&h4[i]);
+            count_key64<XF>(s_hist, (static_cast<uint64_t>(h.x) << 32) | q.x, pd, sub);
+            count_key64<XF>(s_hist, (static_cast<uint64_t>(h.y) << 32) | q.y, pd, sub);
+            count_key64<XF>(s_hist, (static_cast<uint64_t>(h.z) << 32) | q.z, pd, sub);
+            count_key64<XF>(s_hist, (static_cast<uint64_t>(h.w) << 32) | q.w, pd, sub);
+        } else {
+            count_key64<XF>(s_hist, (static_cast<uint64_t>(q.y) << 32) | q.x, pd, sub);
+            count_key64<XF>(s_hist, (static_cast<uint64_t>(q.w) << 32) | q.z, pd, sub);
+        }
+    }
+    if (blockIdx.x == 0 && threadIdx.x < n - nvec * PER_VEC) {
+        const uint32_t j = nvec * PER_VEC + threadIdx.x;
+        const uint64_t key = SOA ? (static_cast<uint64_t>(keys_hi[j]) << 32) | keys[j]
+                                 : (static_cast<uint64_t>(keys[2 * j + 1]) << 32) | keys[2 * j];
+        count_key64<XF>(s_hist, key, pd, sub);
+    }
+    __syncthreads();
+
+    for (uint32_t i = threadIdx.x; i < pd.passes * kRadix; i += kUpBlock) {
+        uint32_t c = 0;
+#pragma unroll
+        for (int s = 0; s < kUpSub64; ++s) c += s_hist[i * kUpSub64 + ((i + s) % kUpSub64)];
         if (c) fetch_add_agent(&bins[i], c);
     }
 }
@@ -213,12 +293,20 @@ __device__ __forceinline__ uint32_t ballot_rank(uint32_t* my_count, uint32_t d, 
     return before + below;
 }
 
-// Arguments of one digit pass.
+// Arguments of one digit pass.  Keys are u32 words, or 8-byte keys (two
+// words, low first) for the 64-bit kernels; with soa_in (soa_out) the 64-bit
+// keys are read from (written to) a low-word array src_keys (dst_keys) and a
+// high-word array src_hi (dst_hi).
 struct PassArgs {
     const uint32_t* src_keys;
     uint32_t* dst_keys;
     const uint32_t* src_vals;
     uint32_t* dst_vals;
+    const uint32_t* src_hi;
+    uint32_t* dst_hi;
+    uint32_t soa_in, soa_out;
+    KeyXform xin;              // applied to the keys as loaded (XF_IN kernels)
+    KeyXform xout;             // applied to the keys as stored (XF_OUT kernels)
     uint32_t n, tiles, shift, width;   // digit = bits [shift, shift + width) of the key
     const uint32_t* bins;      // global digit counts of this pass
     uint32_t* states;          // look-back words of this pass, zeroed
@@ -251,13 +339,42 @@ __device__ __forceinline__ void load_rows(const uint32_t* __restrict__ src, uint
                                                     kNonTemporal);
 }
 
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+
+// The same rows of 8-byte keys: one 8-byte load per lane and row (a row is
+// 512 consecutive bytes); n < 2^29 keeps every byte offset of the array
+// below 2^32.
+template <int ITEMS, int TILE>
+__device__ __forceinline__ void load_rows64(const uint32_t* __restrict__ src, uint32_t tile,
+                                            uint32_t n, uint32_t wave, uint32_t lane,
+                                            uint64_t (&x)[ITEMS]) {
+    const __amdgpu_buffer_rsrc_t r = __builtin_amdgcn_make_buffer_rsrc(
+        const_cast<uint32_t*>(src), 0, static_cast<int>(n * 8u), kBufferWord3);
+    const uint32_t first = (tile * TILE + wave * (kWave * ITEMS) + lane) * 8u;
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        const u32x2 w = __builtin_amdgcn_raw_buffer_load_b64(
+            r, static_cast<int>(first + j * kWave * 8), 0, kNonTemporal);
+        x[j] = (static_cast<uint64_t>(w.y) << 32) | w.x;
+    }
+}
+
+// Digit of a key: bits [shift, shift + width) (a 64-bit key may straddle its words).
+__device__ __forceinline__ uint32_t digit_of(uint32_t k, uint32_t shift, uint32_t width) {
+    return __builtin_amdgcn_ubfe(k, shift, width);
+}
+__device__ __forceinline__ uint32_t digit_of(uint64_t k, uint32_t shift, uint32_t width) {
+    return __builtin_amdgcn_ubfe(static_cast<uint32_t>(k >> shift), 0, width);
+}
+
 // One-sweep pass over one 8-bit digit.  Persistent: each block loops over the
 // tiles the scheduler hands it.  Per tile: load, stable in-wave rank (LDS
 // atomics or ballots), tile counts and scans, decoupled look-back, re-layout
 // in digit order in LDS, scatter of each digit run.
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FLIP_IN, bool FLIP_OUT>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XF_IN, bool XF_OUT, bool KEY64>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
 void onesweep_kernel(PassArgs a) {
+    using Key = typename std::conditional<KEY64, uint64_t, uint32_t>::type;
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
     constexpr int WAVE_KEYS = kWave * ITEMS;
@@ -266,7 +383,8 @@ void onesweep_kernel(PassArgs a) {
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
 
     // One staging buffer: the keys in digit order, then the values in digit order.
-    __shared__ uint32_t s_buf[TILE];
+    __shared__ Key s_buf[TILE];
+    uint32_t* const s_vbuf = reinterpret_cast<uint32_t*>(s_buf);
     __shared__ uint32_t s_off[WAVES * kRadix];   // per-wave digit counters, then offsets
     __shared__ uint32_t s_adjust[kRadix];
     __shared__ uint32_t s_wsum[2][kRadix / kWave];
@@ -313,20 +431,35 @@ void onesweep_kernel(PassArgs a) {
         __syncthreads();
         const uint32_t tile = s_next;
         if (tile >= tiles) break;   // uniform: no tiles left
-        uint32_t k[ITEMS];
-        load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
+        Key k[ITEMS];
+        if constexpr (KEY64) {
+            if (a.soa_in) {
+                uint32_t lo[ITEMS], hi[ITEMS];
+                load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, lo);
+                load_rows<ITEMS, TILE>(a.src_hi, tile, n, wave, lane, hi);
+#pragma unroll
+                for (int j = 0; j < ITEMS; ++j) k[j] = (static_cast<uint64_t>(hi[j]) << 32) | lo[j];
+            } else {
+                load_rows64<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
+            }
+        } else {
+            load_rows<ITEMS, TILE>(src_keys, tile, n, wave, lane, k);
+        }
         const uint32_t tile_base = tile * TILE;
         const uint32_t valid = (n - tile_base < static_cast<uint32_t>(TILE)) ? n - tile_base : TILE;
         const bool full = (valid == static_cast<uint32_t>(TILE));
         const uint32_t first = tile_base + wave * WAVE_KEYS + lane;
-        if (FLIP_IN) {
+        if (XF_IN) {
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) k[j] = float_to_sortable(k[j]);
+            for (int j = 0; j < ITEMS; ++j) {
+                if constexpr (KEY64) k[j] = xform64(k[j], a.xin);
+                else k[j] = xform32(k[j], a.xin);
+            }
         }
         if (!full) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j)
-                if (first + j * kWave >= n) k[j] = 0xFFFFFFFFu;   // padding sorts last
+                if (first + j * kWave >= n) k[j] = ~static_cast<Key>(0);   // padding sorts last
         }
 
         // ---- stable rank inside the wave --------------------------------------
@@ -342,7 +475,7 @@ void onesweep_kernel(PassArgs a) {
             // hardware checks directly and every parity test depends on.
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+                const uint32_t d = digit_of(k[j], shift, width);
                 const uint32_t slot = atomicAdd(&my_count[d], 1u);   // served in lane order
                 if (j % 2 == 0) pos[j / 2] = slot;
                 else pos[j / 2] |= slot << 16;
@@ -350,7 +483,7 @@ void onesweep_kernel(PassArgs a) {
         } else {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
-                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+                const uint32_t d = digit_of(k[j], shift, width);
                 const uint32_t slot = ballot_rank(my_count, d, lane);
                 if (j % 2 == 0) pos[j / 2] = slot;
                 else pos[j / 2] |= slot << 16;
@@ -430,9 +563,9 @@ void onesweep_kernel(PassArgs a) {
         for (int j = 0; j < ITEMS; ++j) {
             // recompute the digit rather than keep the rank loop's LDS addresses
             // alive across the scans (an empty asm hides the reuse)
-            uint32_t key = k[j];
+            Key key = k[j];
             asm volatile("" : "+v"(key));
-            const uint32_t d = __builtin_amdgcn_ubfe(key, shift, width);
+            const uint32_t d = digit_of(key, shift, width);
             // (the clamp never changes a consistent position; it keeps the store in the tile)
             const uint32_t sh = 16 * (j % 2);
             const uint32_t p = min(s_off[wave * kRadix + d] + ((pos[j / 2] >> sh) & 0xFFFFu),
@@ -491,21 +624,37 @@ void onesweep_kernel(PassArgs a) {
         // slots can be in flight together.  A pad's destination can lie past
         // 2^30, where its byte offset would wrap round 2^32 back into the
         // buffer; it is clamped to n first (n * 4 < 2^32 is out of range).
-        const __amdgpu_buffer_rsrc_t out_keys =
-            __builtin_amdgcn_make_buffer_rsrc(dst_keys, 0, static_cast<int>(n * 4u), kBufferWord3);
+        const bool soa_out = KEY64 && a.soa_out;   // uniform
+        const uint32_t key_bytes = (KEY64 && !soa_out) ? 8u : 4u;
+        const __amdgpu_buffer_rsrc_t out_keys = __builtin_amdgcn_make_buffer_rsrc(
+            dst_keys, 0, static_cast<int>(n * key_bytes), kBufferWord3);
+        const __amdgpu_buffer_rsrc_t out_hi = __builtin_amdgcn_make_buffer_rsrc(
+            KEY64 ? a.dst_hi : dst_keys, 0, static_cast<int>(n * 4u), kBufferWord3);
         uint32_t digits[PAIRS ? ITEMS / 4 : 1];
 #pragma unroll
         for (int r = 0; r < ITEMS; ++r) {
             const uint32_t i = r * BLOCK + tid;
-            const uint32_t key = s_buf[i];
-            const uint32_t d = __builtin_amdgcn_ubfe(key, shift, width);
+            Key key = s_buf[i];
+            const uint32_t d = digit_of(key, shift, width);
             if (PAIRS) {
                 if (r % 4 == 0) digits[r / 4] = d;
                 else digits[r / 4] |= d << (8 * (r % 4));
             }
             const uint32_t dst = min(i + s_adjust[d], n);
-            __builtin_amdgcn_raw_buffer_store_b32(FLIP_OUT ? sortable_to_float(key) : key, out_keys,
-                                                  static_cast<int>(dst * 4u), 0, 0);
+            if constexpr (KEY64) {
+                if (XF_OUT) key = xform64(key, a.xout);
+                const uint32_t lo = static_cast<uint32_t>(key), hi = static_cast<uint32_t>(key >> 32);
+                if (soa_out) {
+                    __builtin_amdgcn_raw_buffer_store_b32(lo, out_keys, static_cast<int>(dst * 4u), 0, 0);
+                    __builtin_amdgcn_raw_buffer_store_b32(hi, out_hi, static_cast<int>(dst * 4u), 0, 0);
+                } else {
+                    __builtin_amdgcn_raw_buffer_store_b64(u32x2{lo, hi}, out_keys,
+                                                          static_cast<int>(dst * 8u), 0, 0);
+                }
+            } else {
+                __builtin_amdgcn_raw_buffer_store_b32(XF_OUT ? xform32(key, a.xout) : key, out_keys,
+                                                      static_cast<int>(dst * 4u), 0, 0);
+            }
             if (PAIRS && r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounds live registers
         }
         if (PAIRS) {
@@ -513,14 +662,14 @@ void onesweep_kernel(PassArgs a) {
                 __builtin_amdgcn_make_buffer_rsrc(dst_vals, 0, static_cast<int>(n * 4u), kBufferWord3);
             __syncthreads();   // every key has been read from the staging buffer
 #pragma unroll
-            for (int j = 0; j < ITEMS; ++j) s_buf[(pos[j / 2] >> (16 * (j % 2))) & 0xFFFFu] = v[j];
+            for (int j = 0; j < ITEMS; ++j) s_vbuf[(pos[j / 2] >> (16 * (j % 2))) & 0xFFFFu] = v[j];
             __syncthreads();
 #pragma unroll
             for (int r = 0; r < ITEMS; ++r) {
                 const uint32_t i = r * BLOCK + tid;
                 const uint32_t d = (digits[r / 4] >> (8 * (r % 4))) & 0xFFu;
                 const uint32_t dst = min(i + s_adjust[d], n);
-                __builtin_amdgcn_raw_buffer_store_b32(s_buf[i], out_vals, static_cast<int>(dst * 4u), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32(s_vbuf[i], out_vals, static_cast<int>(dst * 4u), 0, 0);
             }
         }
         // the next iteration rewrites s_buf and s_adjust only after a barrier
@@ -533,16 +682,18 @@ void onesweep_kernel(PassArgs a) {
 // counts, look-back or temp storage.  Pass p re-lays the tile out in the
 // order of digit p; that order is pass p + 1's input order, which is the LSD
 // recurrence of "WebGPU Unleashed", 4.1 (each pass a stable counting sort).
-// Pads (key 0xFFFFFFFF after the flip) fill the tile past n; they carry the
-// last digit of every pass and come after every real key in input order, so
-// they stay at positions n.. in every pass and are never stored.
+// Pads (key 0xFFFFFFFF after the order transform) fill the tile past n;
+// they carry the last digit of every pass and come after every real key in
+// input order, so they stay at positions n.. in every pass and are never
+// stored.  XF: keys are transformed on the way in (pd.xf) and back on the way
+// out (xout).
 // ---------------------------------------------------------------------------
-template <int BLOCK, int ITEMS, bool PAIRS, bool FLIP>
+template <int BLOCK, int ITEMS, bool PAIRS, bool XF>
 __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __restrict__ keys_in,
                                                           uint32_t* __restrict__ keys_out,
                                                           const uint32_t* __restrict__ vals_in,
                                                           uint32_t* __restrict__ vals_out,
-                                                          uint32_t n, PassDigits pd) {
+                                                          uint32_t n, PassDigits pd, KeyXform xout) {
     constexpr int WAVES = BLOCK / kWave;
     constexpr int TILE = BLOCK * ITEMS;
     constexpr int WAVE_KEYS = kWave * ITEMS;
@@ -565,7 +716,7 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
     for (int j = 0; j < ITEMS; ++j) {
         const uint32_t i = first + j * kWave;
         if (i < n) {
-            k[j] = FLIP ? float_to_sortable(keys_in[i]) : keys_in[i];
+            k[j] = XF ? xform32(keys_in[i], pd.xf) : keys_in[i];
             if constexpr (PAIRS) v[j] = vals_in[i];
         } else {
             k[j] = 0xFFFFFFFFu;
@@ -643,21 +794,23 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
     for (int j = 0; j < ITEMS; ++j) {
         const uint32_t i = first + j * kWave;
         if (i < n) {
-            keys_out[i] = FLIP ? sortable_to_float(k[j]) : k[j];
+            keys_out[i] = XF ? xform32(k[j], xout) : k[j];
             if constexpr (PAIRS) vals_out[i] = v[j];
         }
     }
 }
 
 // Temp layout (every piece 256-byte aligned):
-//   bins     [kMaxPasses][256] u32   global digit counts of each pass
-//   sched    [kMaxPasses][64]  u32   tile counters of each pass, one per group (next_chunked_tile)
-//   states0  [tiles][256]      u32   look-back states of even passes
-//   states1  [tiles][256]      u32   look-back states of odd passes (passes >= 2)
-//   tmp_keys [n] u32, tmp_vals [n] u32   ping-pong buffers (passes >= 2)
+//   bins     [P][256]   u32   global digit counts of each pass (P = 4, or 8 for 64-bit keys)
+//   sched    [P][64]    u32   tile counters of each pass, one per group (next_chunked_tile)
+//   states0  [tiles][256] u32 look-back states of even passes
+//   states1  [tiles][256] u32 look-back states of odd passes (passes >= 2)
+//   tmp_keys [n] keys, tmp_vals [n] u32   ping-pong buffers (passes >= 2)
+//   tmp_keys2 [n] keys   second key buffer of a two-key sort (its outputs are
+//                        two word arrays, so its passes ping-pong in temp)
 // bins, sched and states0 are contiguous and cleared by one fill launch.
 struct SortLayout {
-    size_t bins, sched, states0, states1, tmp_keys, tmp_vals, total;
+    size_t bins, sched, states0, states1, tmp_keys, tmp_vals, tmp_keys2, total;
     uint64_t clear_words;
     uint32_t tiles;
 };
@@ -665,9 +818,10 @@ struct SortLayout {
 constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
 constexpr uint32_t kMaxResidentBlocks = 4096;  // cap on the blocks of one pass
 
-enum class PassShape { kSmall, kPairsLarge, kPairsHuge, kKeysLarge, kKeysHuge };
+enum class PassShape { kSmall, kPairsLarge, kPairsHuge, kKeysLarge, kKeysHuge, kKey64 };
 
-PassShape pass_shape(uint64_t n, bool pairs) {
+PassShape pass_shape(uint64_t n, bool pairs, bool key64) {
+    if (key64) return PassShape::kKey64;
     if (pairs) {
         if (n >= kPairsHugeMinN) return PassShape::kPairsHuge;
         return n >= kPairsLargeMinN ? PassShape::kPairsLarge : PassShape::kSmall;
@@ -677,35 +831,40 @@ PassShape pass_shape(uint64_t n, bool pairs) {
 }
 
 // Keys per tile of the one-sweep pass.
-uint64_t pass_tile_keys(uint64_t n, bool pairs) {
-    switch (pass_shape(n, pairs)) {
+uint64_t pass_tile_keys(uint64_t n, bool pairs, bool key64) {
+    switch (pass_shape(n, pairs, key64)) {
     case PassShape::kPairsLarge: return static_cast<uint64_t>(kPairsBlock) * kPairsItems;
     case PassShape::kPairsHuge: return static_cast<uint64_t>(kPairsBlock) * kPairsHugeItems;
     case PassShape::kKeysLarge: return static_cast<uint64_t>(kKeysBlock) * kKeysItems;
     case PassShape::kKeysHuge: return static_cast<uint64_t>(kKeysHugeBlock) * kKeysItems;
+    case PassShape::kKey64: return static_cast<uint64_t>(kKey64Block) * kKey64Items;
     default: return static_cast<uint64_t>(kSortTile);
     }
 }
 
-SortLayout sort_layout(uint64_t n, bool pairs, int passes) {
+SortLayout sort_layout(uint64_t n, bool pairs, const SortKind& kind) {
     SortLayout L{};
-    const uint64_t tile_keys = pass_tile_keys(n, pairs);
+    const int max_passes = kind.key64 ? kMaxPasses64 : kMaxPasses;
+    const size_t key_bytes = kind.key64 ? 8 : 4;
+    const uint64_t tile_keys = pass_tile_keys(n, pairs, kind.key64);
     L.tiles = static_cast<uint32_t>((n + tile_keys - 1) / tile_keys);
     const size_t states_bytes = align_up(static_cast<size_t>(L.tiles) * kRadix * 4);
     size_t off = 0;
     L.bins = off;
-    off += align_up(kMaxPasses * kRadix * 4);
+    off += align_up(static_cast<size_t>(max_passes) * kRadix * 4);
     L.sched = off;
-    off += static_cast<size_t>(kMaxPasses) * kSchedWords * 4;
+    off += static_cast<size_t>(max_passes) * kSchedWords * 4;
     L.states0 = off;
     off += states_bytes;
     L.clear_words = off / 4;
     L.states1 = off;
-    if (passes >= 2) off += states_bytes;
+    off += states_bytes;   // every sort path has at least two passes' worth of states
     L.tmp_keys = off;
-    if (passes >= 2) off += align_up(n * 4);
+    off += align_up(n * key_bytes);
     L.tmp_vals = off;
-    if (passes >= 2 && pairs) off += align_up(n * 4);
+    if (pairs) off += align_up(n * 4);
+    L.tmp_keys2 = off;
+    if (kind.soa) off += align_up(n * key_bytes);
     L.total = off;
     return L;
 }
@@ -721,9 +880,9 @@ uint32_t resident_blocks(K kernel, int block) {
     return r < kMaxResidentBlocks ? r : kMaxResidentBlocks;
 }
 
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool FI, bool FO>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XI, bool XO, bool KEY64>
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
-    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, FI, FO>;
+    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, XI, XO, KEY64>;
     static const uint32_t resident = resident_blocks(kern, BLOCK);   // one-time init
     const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
@@ -733,51 +892,55 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS>
-hipError_t launch_pass_items(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    if (flip_in && flip_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, true>(a, s);
-    if (flip_in) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, false>(a, s);
-    if (flip_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, true>(a, s);
-    return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false>(a, s);
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool KEY64 = false>
+hipError_t launch_pass_items(bool xf_in, bool xf_out, const PassArgs& a, hipStream_t s) {
+    if (xf_in && xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, true, KEY64>(a, s);
+    if (xf_in) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, false, KEY64>(a, s);
+    if (xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, true, KEY64>(a, s);
+    return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false, KEY64>(a, s);
 }
 
 template <bool PAIRS>
-hipError_t launch_pass(bool flip_in, bool flip_out, const PassArgs& a, hipStream_t s) {
-    const PassShape shape = pass_shape(a.n, PAIRS);
+hipError_t launch_pass(bool xf_in, bool xf_out, bool key64, const PassArgs& a, hipStream_t s) {
+    const PassShape shape = pass_shape(a.n, PAIRS, key64);
+    if (shape == PassShape::kKey64)
+        return launch_pass_items<kKey64Block, kKey64Items, kSortLookback, PAIRS, true>(xf_in, xf_out, a, s);
     if (shape != PassShape::kSmall) {
         if constexpr (PAIRS) {
             if (shape == PassShape::kPairsHuge)
-                return launch_pass_items<kPairsBlock, kPairsHugeItems, kPairsLookback, true>(flip_in, flip_out, a,
+                return launch_pass_items<kPairsBlock, kPairsHugeItems, kPairsLookback, true>(xf_in, xf_out, a,
                                                                                              s);
-            return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(flip_in, flip_out, a, s);
+            return launch_pass_items<kPairsBlock, kPairsItems, kPairsLookback, true>(xf_in, xf_out, a, s);
         } else {
             if (shape == PassShape::kKeysHuge)
-                return launch_pass_items<kKeysHugeBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
-            return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(flip_in, flip_out, a, s);
+                return launch_pass_items<kKeysHugeBlock, kKeysItems, kSortLookback, false>(xf_in, xf_out, a, s);
+            return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(xf_in, xf_out, a, s);
         }
     }
-    return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(flip_in, flip_out, a, s);
+    return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(xf_in, xf_out, a, s);
 }
 
 template <int BLOCK, int ITEMS, bool PAIRS>
 void launch_tile_sort_t(const uint32_t* ki, uint32_t* ko, const uint32_t* vi, uint32_t* vo,
-                        uint32_t n, const PassDigits& pd, bool flip, hipStream_t s) {
-    if (flip)
-        tile_sort_kernel<BLOCK, ITEMS, PAIRS, true><<<1, BLOCK, 0, s>>>(ki, ko, vi, vo, n, pd);
+                        uint32_t n, const PassDigits& pd, bool xf, const KeyXform& xout,
+                        hipStream_t s) {
+    if (xf)
+        tile_sort_kernel<BLOCK, ITEMS, PAIRS, true><<<1, BLOCK, 0, s>>>(ki, ko, vi, vo, n, pd, xout);
     else
-        tile_sort_kernel<BLOCK, ITEMS, PAIRS, false><<<1, BLOCK, 0, s>>>(ki, ko, vi, vo, n, pd);
+        tile_sort_kernel<BLOCK, ITEMS, PAIRS, false><<<1, BLOCK, 0, s>>>(ki, ko, vi, vo, n, pd, xout);
 }
 
 // One block, the smallest tile shape that holds n keys.
 template <bool PAIRS>
 void launch_tile_sort(const uint32_t* ki, uint32_t* ko, const uint32_t* vi, uint32_t* vo,
-                      uint32_t n, const PassDigits& pd, bool flip, hipStream_t s) {
+                      uint32_t n, const PassDigits& pd, bool xf, const KeyXform& xout,
+                      hipStream_t s) {
     if (n <= 256 * 4)
-        launch_tile_sort_t<256, 4, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+        launch_tile_sort_t<256, 4, PAIRS>(ki, ko, vi, vo, n, pd, xf, xout, s);
     else if (n <= 512 * 8)
-        launch_tile_sort_t<512, 8, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+        launch_tile_sort_t<512, 8, PAIRS>(ki, ko, vi, vo, n, pd, xf, xout, s);
     else
-        launch_tile_sort_t<1024, 16, PAIRS>(ki, ko, vi, vo, n, pd, flip, s);
+        launch_tile_sort_t<1024, 16, PAIRS>(ki, ko, vi, vo, n, pd, xf, xout, s);
 }
 
 int upsweep_grid(uint32_t n) {
@@ -787,6 +950,45 @@ int upsweep_grid(uint32_t n) {
     if (g < 1) g = 1;
     if (g > static_cast<uint64_t>(cus)) g = static_cast<uint64_t>(cus);   // one 128 KB block per CU
     return static_cast<int>(g);
+}
+
+// Digit positions of every pass over [begin_bit, end_bit), and the forward transform.
+PassDigits pass_digits(int begin_bit, int end_bit, const KeyXform& xf) {
+    PassDigits pd{};
+    const int passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
+    pd.passes = static_cast<uint32_t>(passes);
+    for (int p = 0; p < passes; ++p) {
+        const int s = begin_bit + kRadixBits * p;
+        const int w = (end_bit - s < kRadixBits) ? end_bit - s : kRadixBits;
+        pd.shift[p] = static_cast<uint32_t>(s);
+        pd.mask[p] = (1u << w) - 1u;
+        pd.width[p] = static_cast<uint32_t>(w);
+    }
+    pd.xf = xf;
+    return pd;
+}
+
+hipError_t launch_upsweep(const SortIo& io, const SortKind& kind, const PassDigits& pd,
+                          uint32_t* bins, hipStream_t stream) {
+    const uint32_t n = io.n;
+    const bool xf = kind.transforms;
+    timing_before(stream, RS_KERNEL_UPSWEEP);
+    const int grid = upsweep_grid(kind.key64 && !kind.soa ? 2 * n : n);
+    if (kind.key64) {
+        if (kind.soa) {
+            if (xf) upsweep64_kernel<true, true><<<grid, kUpBlock, 0, stream>>>(io.keys_in, io.hi_in, n, pd, bins);
+            else upsweep64_kernel<false, true><<<grid, kUpBlock, 0, stream>>>(io.keys_in, io.hi_in, n, pd, bins);
+        } else {
+            if (xf) upsweep64_kernel<true, false><<<grid, kUpBlock, 0, stream>>>(io.keys_in, nullptr, n, pd, bins);
+            else upsweep64_kernel<false, false><<<grid, kUpBlock, 0, stream>>>(io.keys_in, nullptr, n, pd, bins);
+        }
+    } else {
+        if (xf) upsweep_kernel<true><<<grid, kUpBlock, 0, stream>>>(io.keys_in, n, pd, bins);
+        else upsweep_kernel<false><<<grid, kUpBlock, 0, stream>>>(io.keys_in, n, pd, bins);
+    }
+    const hipError_t e = hipGetLastError();
+    timing_after(stream);
+    return e;
 }
 
 }  // namespace
@@ -818,9 +1020,9 @@ int device_cus() {
     return cus;
 }
 
-size_t sort_temp_bytes(uint64_t n, bool pairs, int passes) {
-    if (n <= kTileSortMax) return kAlign;   // the one-block sort needs no temp storage
-    return sort_layout(n, pairs, passes).total;
+size_t sort_temp_bytes(uint64_t n, bool pairs, const SortKind& kind) {
+    if (n <= kTileSortMax && !kind.key64) return kAlign;   // the one-block sort needs no temp storage
+    return sort_layout(n, pairs, kind).total;
 }
 
 hipError_t launch_fill_zero(uint32_t* p, uint64_t words, hipStream_t stream, int kernel_id) {
@@ -835,31 +1037,43 @@ hipError_t launch_fill_zero(uint32_t* p, uint64_t words, hipStream_t stream, int
     return e;
 }
 
-hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32_t* vals_in,
-                       uint32_t* vals_out, uint32_t n, int begin_bit, int end_bit, bool is_f32,
+// Inverse of a forward transform: the same form, with the masks of the two
+// signs swapped when the forward masks flip the sign bit (then the sign of
+// the transformed word is the opposite of the key's).
+KeyXform inverse_xform(const KeyXform& f) {
+    if ((f.pos_hi >> 31) == 0) return f;
+    return KeyXform{f.neg_hi, f.pos_hi, f.neg_lo, f.pos_lo};
+}
+
+hipError_t launch_digit_counts(const SortIo& io, const SortKind& kind, int begin_bit, int end_bit,
+                               uint32_t* d_counts, hipStream_t stream) {
+    const PassDigits pd = pass_digits(begin_bit, end_bit, kind.xf);
+    hipError_t e = launch_fill_zero(d_counts, static_cast<uint64_t>(pd.passes) * kRadix, stream,
+                                    RS_KERNEL_SORT_INIT);
+    if (e != hipSuccess) return e;
+    return launch_upsweep(io, kind, pd, d_counts, stream);
+}
+
+hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, int end_bit,
                        void* temp, hipStream_t stream) {
-    const bool pairs = vals_in != nullptr;
-    const int passes = (end_bit - begin_bit + kRadixBits - 1) / kRadixBits;
-    PassDigits pd{};
-    pd.passes = static_cast<uint32_t>(passes);
-    for (int p = 0; p < passes; ++p) {
-        const int s = begin_bit + kRadixBits * p;
-        const int w = (end_bit - s < kRadixBits) ? end_bit - s : kRadixBits;
-        pd.shift[p] = static_cast<uint32_t>(s);
-        pd.mask[p] = (1u << w) - 1u;
-        pd.width[p] = static_cast<uint32_t>(w);
-    }
-    if (n <= kTileSortMax) {
+    const uint32_t n = io.n;
+    const bool pairs = io.vals_in != nullptr;
+    const PassDigits pd = pass_digits(begin_bit, end_bit, kind.xf);
+    const int passes = static_cast<int>(pd.passes);
+    const KeyXform xout = inverse_xform(kind.xf);
+    if (n <= kTileSortMax && !kind.key64) {
         timing_before(stream, RS_KERNEL_TILE_SORT);
         if (pairs)
-            launch_tile_sort<true>(keys_in, keys_out, vals_in, vals_out, n, pd, is_f32, stream);
+            launch_tile_sort<true>(io.keys_in, io.keys_out, io.vals_in, io.vals_out, n, pd, kind.transforms,
+                                   xout, stream);
         else
-            launch_tile_sort<false>(keys_in, keys_out, nullptr, nullptr, n, pd, is_f32, stream);
+            launch_tile_sort<false>(io.keys_in, io.keys_out, nullptr, nullptr, n, pd, kind.transforms, xout,
+                                    stream);
         const hipError_t e = hipGetLastError();
         timing_after(stream);
         return e;
     }
-    const SortLayout L = sort_layout(n, pairs, passes);
+    const SortLayout L = sort_layout(n, pairs, kind);
     char* base = static_cast<char*>(temp);
     uint32_t* bins = reinterpret_cast<uint32_t*>(base + L.bins);
     uint32_t* sched = reinterpret_cast<uint32_t*>(base + L.sched);
@@ -867,29 +1081,34 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
                            reinterpret_cast<uint32_t*>(base + L.states1)};
     uint32_t* tmp_keys = reinterpret_cast<uint32_t*>(base + L.tmp_keys);
     uint32_t* tmp_vals = reinterpret_cast<uint32_t*>(base + L.tmp_vals);
+    uint32_t* tmp_keys2 = reinterpret_cast<uint32_t*>(base + L.tmp_keys2);
 
     hipError_t e = launch_fill_zero(reinterpret_cast<uint32_t*>(base), L.clear_words, stream,
                                     RS_KERNEL_SORT_INIT);
     if (e != hipSuccess) return e;
-
-    timing_before(stream, RS_KERNEL_UPSWEEP);
-    if (is_f32)
-        upsweep_kernel<true><<<upsweep_grid(n), kUpBlock, 0, stream>>>(keys_in, n, pd, bins);
-    else
-        upsweep_kernel<false><<<upsweep_grid(n), kUpBlock, 0, stream>>>(keys_in, n, pd, bins);
-    e = hipGetLastError();
-    timing_after(stream);
+    e = launch_upsweep(io, kind, pd, bins, stream);
     if (e != hipSuccess) return e;
 
-    const uint32_t* sk = keys_in;
-    const uint32_t* sv = vals_in;
+    const uint32_t* sk = io.keys_in;
+    const uint32_t* sv = io.vals_in;
     for (int p = 0; p < passes; ++p) {
+        const bool last = p == passes - 1;
         const bool to_out = ((passes - 1 - p) % 2) == 0;
         PassArgs a{};
         a.src_keys = sk;
-        a.dst_keys = to_out ? keys_out : tmp_keys;
         a.src_vals = sv;
-        a.dst_vals = pairs ? (to_out ? vals_out : tmp_vals) : nullptr;
+        a.dst_vals = pairs ? (to_out ? io.vals_out : tmp_vals) : nullptr;
+        if (kind.soa) {
+            // two-key sort: the first pass reads the two word arrays, the last
+            // writes them; in between 8-byte keys ping-pong in temp
+            a.soa_in = (p == 0);
+            a.src_hi = io.hi_in;
+            a.soa_out = last;
+            a.dst_keys = last ? io.keys_out : ((p % 2 == 0) ? tmp_keys : tmp_keys2);
+            a.dst_hi = io.hi_out;
+        } else {
+            a.dst_keys = to_out ? io.keys_out : tmp_keys;
+        }
         a.n = n;
         a.tiles = L.tiles;
         a.shift = pd.shift[p];
@@ -902,11 +1121,13 @@ hipError_t launch_sort(const uint32_t* keys_in, uint32_t* keys_out, const uint32
         // gathered equal digits into runs, so its atomic rank pays off up to a
         // digit holding half of the keys (measured); later passes stop at 1/16.
         a.atomic_limit_log2 = (p == 0) ? 1u : 4u;
-        const bool flip_in = is_f32 && p == 0;
-        const bool flip_out = is_f32 && p == passes - 1;
+        a.xin = kind.xf;
+        a.xout = xout;
+        const bool xf_in = kind.transforms && p == 0;
+        const bool xf_out = kind.transforms && last;
         timing_before(stream, RS_KERNEL_ONESWEEP);
-        e = pairs ? launch_pass<true>(flip_in, flip_out, a, stream)
-                  : launch_pass<false>(flip_in, flip_out, a, stream);
+        e = pairs ? launch_pass<true>(xf_in, xf_out, kind.key64, a, stream)
+                  : launch_pass<false>(xf_in, xf_out, kind.key64, a, stream);
         timing_after(stream);
         if (e != hipSuccess) return e;
         sk = a.dst_keys;

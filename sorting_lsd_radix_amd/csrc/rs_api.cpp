@@ -13,8 +13,6 @@ namespace rs {
 
 namespace {
 
-constexpr int kMaxPasses = 4;
-
 struct Range {
     uintptr_t lo, hi;
 };
@@ -57,26 +55,79 @@ void clear_timing_locked() {
     g_timing.clear();
 }
 
-rs_status sort_common(const uint32_t* keys_in, uint32_t* keys_out, const uint32_t* vals_in,
+bool key_type_ok(int t) { return t >= RS_KEY_U32 && t <= RS_KEY_F64; }
+bool is_key64(int t) { return t >= RS_KEY_U64; }
+
+// Forward order transform of a key type and direction (see KeyXform).
+KeyXform forward_xform(int key_type, bool descending) {
+    KeyXform x{0u, 0u, 0u, 0u};
+    switch (key_type) {
+    case RS_KEY_I32:
+    case RS_KEY_I64:
+        x.pos_hi = x.neg_hi = 0x80000000u;   // flip the sign bit
+        break;
+    case RS_KEY_F32:
+        x.pos_hi = 0x80000000u;              // non-negative: set the sign bit
+        x.neg_hi = 0xFFFFFFFFu;              // negative: flip every bit
+        break;
+    case RS_KEY_F64:
+        x.pos_hi = 0x80000000u;
+        x.neg_hi = 0xFFFFFFFFu;
+        x.neg_lo = 0xFFFFFFFFu;
+        break;
+    default:
+        break;
+    }
+    if (descending) {   // the complement reverses the order
+        x.pos_hi = ~x.pos_hi;
+        x.neg_hi = ~x.neg_hi;
+        x.pos_lo = ~x.pos_lo;
+        x.neg_lo = ~x.neg_lo;
+    }
+    return x;
+}
+
+SortKind sort_kind(int key_type, bool descending, bool soa) {
+    SortKind k{};
+    k.key64 = is_key64(key_type) || soa;
+    k.soa = soa;
+    k.xf = forward_xform(key_type, descending);
+    k.transforms = k.xf.pos_hi || k.xf.neg_hi || (k.key64 && (k.xf.pos_lo || k.xf.neg_lo));
+    return k;
+}
+
+// One sort call: keys_in/keys_out are u32 or u64 arrays (soa: the minor /
+// low-word arrays, with hi_in/hi_out the major arrays).
+rs_status sort_common(int key_type, bool descending, bool soa, const void* keys_in, void* keys_out,
+                      const uint32_t* hi_in, uint32_t* hi_out, const uint32_t* vals_in,
                       uint32_t* vals_out, uint64_t n, int begin_bit, int end_bit, void* d_temp,
-                      size_t* temp_bytes, hipStream_t stream, bool pairs, bool is_f32) {
+                      size_t* temp_bytes, hipStream_t stream, bool pairs) {
     if (temp_bytes == nullptr) return RS_ERR_INVALID_VALUE;
-    if (bad_bits(begin_bit, end_bit)) return RS_ERR_INVALID_VALUE;
-    if (n >= RS_MAX_N) return RS_ERR_UNSUPPORTED_SIZE;
-    const size_t need = sort_temp_bytes(n, pairs, kMaxPasses);
+    if (!key_type_ok(key_type)) return RS_ERR_INVALID_VALUE;
+    const SortKind kind = sort_kind(key_type, descending, soa);
+    const int key_bits = kind.key64 ? 64 : 32;
+    if (begin_bit < 0 || end_bit > key_bits || begin_bit > end_bit) return RS_ERR_INVALID_VALUE;
+    if (n >= (kind.key64 ? RS_MAX_N64 : RS_MAX_N)) return RS_ERR_UNSUPPORTED_SIZE;
+    const size_t need = sort_temp_bytes(n, pairs, kind);
     if (d_temp == nullptr) {
         *temp_bytes = need;
         return RS_OK;
     }
     if (n == 0) return RS_OK;
     if (keys_in == nullptr || keys_out == nullptr) return RS_ERR_INVALID_VALUE;
+    if (soa && (hi_in == nullptr || hi_out == nullptr)) return RS_ERR_INVALID_VALUE;
     if (pairs && (vals_in == nullptr || vals_out == nullptr)) return RS_ERR_INVALID_VALUE;
-    if (!aligned16(keys_in) || !aligned16(keys_out) || !aligned16(d_temp))
-        return RS_ERR_MISALIGNED;
+    if (!aligned16(keys_in) || !aligned16(keys_out) || !aligned16(d_temp)) return RS_ERR_MISALIGNED;
+    if (soa && (!aligned16(hi_in) || !aligned16(hi_out))) return RS_ERR_MISALIGNED;
     if (pairs && (!aligned16(vals_in) || !aligned16(vals_out))) return RS_ERR_MISALIGNED;
     if (*temp_bytes < need) return RS_ERR_TEMP_TOO_SMALL;
-    std::vector<Range> rs{range_of(keys_in, n * 4), range_of(keys_out, n * 4),
+    const size_t key_bytes = (kind.key64 && !soa) ? 8 : 4;
+    std::vector<Range> rs{range_of(keys_in, n * key_bytes), range_of(keys_out, n * key_bytes),
                           range_of(d_temp, need)};
+    if (soa) {
+        rs.push_back(range_of(hi_in, n * 4));
+        rs.push_back(range_of(hi_out, n * 4));
+    }
     if (pairs) {
         rs.push_back(range_of(vals_in, n * 4));
         rs.push_back(range_of(vals_out, n * 4));
@@ -88,13 +139,16 @@ rs_status sort_common(const uint32_t* keys_in, uint32_t* keys_out, const uint32_
         // an empty ordering field: every key compares equal, the stable
         // order is the input order
         timing_before(stream, RS_KERNEL_COPY);
-        e = hipMemcpyAsync(keys_out, keys_in, n * 4, hipMemcpyDeviceToDevice, stream);
+        e = hipMemcpyAsync(keys_out, keys_in, n * key_bytes, hipMemcpyDeviceToDevice, stream);
+        if (e == hipSuccess && soa)
+            e = hipMemcpyAsync(hi_out, hi_in, n * 4, hipMemcpyDeviceToDevice, stream);
         if (e == hipSuccess && pairs)
             e = hipMemcpyAsync(vals_out, vals_in, n * 4, hipMemcpyDeviceToDevice, stream);
         timing_after(stream);
     } else {
-        e = launch_sort(keys_in, keys_out, pairs ? vals_in : nullptr, pairs ? vals_out : nullptr,
-                        static_cast<uint32_t>(n), begin_bit, end_bit, is_f32, d_temp, stream);
+        SortIo io{static_cast<const uint32_t*>(keys_in), static_cast<uint32_t*>(keys_out), hi_in, hi_out,
+                  pairs ? vals_in : nullptr, pairs ? vals_out : nullptr, static_cast<uint32_t>(n)};
+        e = launch_sort(io, kind, begin_bit, end_bit, d_temp, stream);
     }
     return e == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
@@ -129,23 +183,67 @@ extern "C" {
 
 rs_status rs_sort_keys_u32(const uint32_t* keys_in, uint32_t* keys_out, uint64_t n, int begin_bit,
                            int end_bit, void* d_temp, size_t* temp_bytes, hipStream_t stream) {
-    return rs::sort_common(keys_in, keys_out, nullptr, nullptr, n, begin_bit, end_bit, d_temp,
-                           temp_bytes, stream, false, false);
+    return rs::sort_common(RS_KEY_U32, false, false, keys_in, keys_out, nullptr, nullptr, nullptr,
+                           nullptr, n, begin_bit, end_bit, d_temp, temp_bytes, stream, false);
 }
 
 rs_status rs_sort_pairs_u32(const uint32_t* keys_in, uint32_t* keys_out, const uint32_t* vals_in,
                             uint32_t* vals_out, uint64_t n, int begin_bit, int end_bit,
                             void* d_temp, size_t* temp_bytes, hipStream_t stream) {
-    return rs::sort_common(keys_in, keys_out, vals_in, vals_out, n, begin_bit, end_bit, d_temp,
-                           temp_bytes, stream, true, false);
+    return rs::sort_common(RS_KEY_U32, false, false, keys_in, keys_out, nullptr, nullptr, vals_in,
+                           vals_out, n, begin_bit, end_bit, d_temp, temp_bytes, stream, true);
 }
 
 rs_status rs_sort_pairs_f32(const float* keys_in, float* keys_out, const uint32_t* vals_in,
                             uint32_t* vals_out, uint64_t n, int begin_bit, int end_bit,
                             void* d_temp, size_t* temp_bytes, hipStream_t stream) {
-    return rs::sort_common(reinterpret_cast<const uint32_t*>(keys_in),
-                           reinterpret_cast<uint32_t*>(keys_out), vals_in, vals_out, n, begin_bit,
-                           end_bit, d_temp, temp_bytes, stream, true, true);
+    return rs::sort_common(RS_KEY_F32, false, false, keys_in, keys_out, nullptr, nullptr, vals_in,
+                           vals_out, n, begin_bit, end_bit, d_temp, temp_bytes, stream, true);
+}
+
+rs_status rs_sort_keys(rs_key_type key_type, int descending, const void* keys_in, void* keys_out,
+                       uint64_t n, int begin_bit, int end_bit, void* d_temp, size_t* temp_bytes,
+                       hipStream_t stream) {
+    return rs::sort_common(key_type, descending != 0, false, keys_in, keys_out, nullptr, nullptr,
+                           nullptr, nullptr, n, begin_bit, end_bit, d_temp, temp_bytes, stream, false);
+}
+
+rs_status rs_sort_pairs(rs_key_type key_type, int descending, const void* keys_in, void* keys_out,
+                        const uint32_t* vals_in, uint32_t* vals_out, uint64_t n, int begin_bit,
+                        int end_bit, void* d_temp, size_t* temp_bytes, hipStream_t stream) {
+    return rs::sort_common(key_type, descending != 0, false, keys_in, keys_out, nullptr, nullptr,
+                           vals_in, vals_out, n, begin_bit, end_bit, d_temp, temp_bytes, stream, true);
+}
+
+rs_status rs_sort_two_keys_u32(const uint32_t* major_in, const uint32_t* minor_in,
+                               uint32_t* major_out, uint32_t* minor_out, const uint32_t* vals_in,
+                               uint32_t* vals_out, uint64_t n, void* d_temp, size_t* temp_bytes,
+                               hipStream_t stream) {
+    if ((vals_in == nullptr) != (vals_out == nullptr)) return RS_ERR_INVALID_VALUE;
+    return rs::sort_common(RS_KEY_U64, false, true, minor_in, minor_out, major_in, major_out,
+                           vals_in, vals_out, n, 0, 64, d_temp, temp_bytes, stream,
+                           vals_in != nullptr);
+}
+
+rs_status rs_digit_counts(rs_key_type key_type, int descending, const void* keys, uint64_t n,
+                          int begin_bit, int end_bit, uint32_t* d_counts, hipStream_t stream) {
+    using namespace rs;
+    if (!key_type_ok(key_type)) return RS_ERR_INVALID_VALUE;
+    const SortKind kind = sort_kind(key_type, descending != 0, false);
+    const int key_bits = kind.key64 ? 64 : 32;
+    if (begin_bit < 0 || end_bit > key_bits || begin_bit > end_bit) return RS_ERR_INVALID_VALUE;
+    if (n >= (kind.key64 ? RS_MAX_N64 : RS_MAX_N)) return RS_ERR_UNSUPPORTED_SIZE;
+    if (begin_bit == end_bit) return RS_OK;   // no passes, nothing to count
+    if (d_counts == nullptr || (n > 0 && keys == nullptr)) return RS_ERR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(d_counts) & 3u) != 0) return RS_ERR_MISALIGNED;
+    if (n > 0 && !aligned16(keys)) return RS_ERR_MISALIGNED;
+    const size_t passes = static_cast<size_t>(end_bit - begin_bit + 7) / 8;
+    if (n > 0 && overlaps({range_of(keys, n * (kind.key64 ? 8 : 4)), range_of(d_counts, passes * 1024)}))
+        return RS_ERR_OVERLAP;
+    SortIo io{static_cast<const uint32_t*>(keys), nullptr, nullptr, nullptr, nullptr, nullptr,
+              static_cast<uint32_t>(n)};
+    const hipError_t e = launch_digit_counts(io, kind, begin_bit, end_bit, d_counts, stream);
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 
 rs_status rs_compact_positive_f32(const float* in, float* out, uint32_t* d_count, uint64_t n,
@@ -197,7 +295,8 @@ const char* rs_status_string(rs_status status) {
     switch (status) {
         case RS_OK: return "RS_OK: success";
         case RS_ERR_INVALID_VALUE: return "RS_ERR_INVALID_VALUE: invalid argument";
-        case RS_ERR_UNSUPPORTED_SIZE: return "RS_ERR_UNSUPPORTED_SIZE: n must be below 2^30";
+        case RS_ERR_UNSUPPORTED_SIZE:
+            return "RS_ERR_UNSUPPORTED_SIZE: n must be below 2^30 (2^29 for 64-bit and two-key sorts)";
         case RS_ERR_TEMP_TOO_SMALL: return "RS_ERR_TEMP_TOO_SMALL: temporary buffer too small";
         case RS_ERR_OVERLAP: return "RS_ERR_OVERLAP: buffers overlap";
         case RS_ERR_MISALIGNED: return "RS_ERR_MISALIGNED: pointer not 16-byte aligned";

@@ -89,3 +89,71 @@ def gpu_bitonic(keys, tile, b=0, e=32):
     k = host(ko)
     assert np.array_equal(host(tk), keys), "input modified"
     return k
+
+
+_TORCH_OF = {np.uint32: torch.uint32, np.int32: torch.int32, np.float32: torch.float32,
+             np.uint64: torch.uint64, np.int64: torch.int64, np.float64: torch.float64}
+_KEY_TYPE = {np.uint32: rs.RS_KEY_U32, np.int32: rs.RS_KEY_I32, np.float32: rs.RS_KEY_F32,
+             np.uint64: rs.RS_KEY_U64, np.int64: rs.RS_KEY_I64, np.float64: rs.RS_KEY_F64}
+
+
+def _raw(a):
+    """Bit patterns of a typed array (unsigned view of the same width)."""
+    return a.view(np.uint32 if a.dtype.itemsize == 4 else np.uint64)
+
+
+def poisoned_like(keys):
+    """A device array of the keys' type filled with 0xDE bytes."""
+    t = torch.full((max(keys.size, 0) * keys.dtype.itemsize,), 0xDE, dtype=torch.uint8, device=DEV)
+    return t.view(_TORCH_OF[keys.dtype.type])
+
+
+def gpu_sort_typed(keys, vals=None, descending=False, b=0, e=None, temp=None):
+    """rs_sort_keys / rs_sort_pairs on a typed numpy array; returns keys or (keys, vals)."""
+    n = keys.size
+    kt = _KEY_TYPE[keys.dtype.type]
+    e = keys.dtype.itemsize * 8 if e is None else e
+    tk = to_dev(keys)
+    ko = poisoned_like(keys)
+    if vals is None:
+        need = rs.rs_sort_keys(kt, descending, None, None, n, b, e, None, 0)
+        temp = temp_for(need) if temp is None else temp
+        rs.rs_sort_keys(kt, descending, tk, ko, n, b, e, temp, temp.numel())
+        k = host(ko)
+        assert np.array_equal(_raw(host(tk)), _raw(keys)), "input modified"
+        return k
+    tv = to_dev(vals)
+    vo = poisoned(n)
+    need = rs.rs_sort_pairs(kt, descending, None, None, None, None, n, b, e, None, 0)
+    temp = temp_for(need) if temp is None else temp
+    rs.rs_sort_pairs(kt, descending, tk, ko, tv, vo, n, b, e, temp, temp.numel())
+    k, v = host(ko), host(vo)
+    assert np.array_equal(_raw(host(tk)), _raw(keys)) and np.array_equal(host(tv), vals), \
+        "input modified"
+    return k, v
+
+
+def gpu_sort_two_keys(major, minor, vals=None, temp=None):
+    """rs_sort_two_keys_u32; returns (major, minor) or (major, minor, vals)."""
+    n = major.size
+    tm, tn = to_dev(major), to_dev(minor)
+    mo, no = poisoned(n), poisoned(n)
+    tv = to_dev(vals) if vals is not None else None
+    vo = poisoned(n) if vals is not None else None
+    need = rs.rs_sort_two_keys_u32(None, None, None, None, None, None, n, None, 0)
+    temp = temp_for(need) if temp is None else temp
+    rs.rs_sort_two_keys_u32(tm, tn, mo, no, tv, vo, n, temp, temp.numel())
+    out = (host(mo), host(no)) if vals is None else (host(mo), host(no), host(vo))
+    assert np.array_equal(host(tm), major) and np.array_equal(host(tn), minor), "input modified"
+    return out
+
+
+def gpu_digit_counts(keys, descending=False, b=0, e=None):
+    """rs_digit_counts on a typed numpy array: uint32 [passes, 256]."""
+    kt = _KEY_TYPE[keys.dtype.type]
+    e = keys.dtype.itemsize * 8 if e is None else e
+    passes = (e - b + 7) // 8
+    tk = to_dev(keys)
+    counts = poisoned(max(passes, 1) * 256)
+    rs.rs_digit_counts(kt, descending, tk, keys.size, b, e, counts)
+    return host(counts)[: passes * 256].reshape(passes, 256)

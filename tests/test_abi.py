@@ -139,3 +139,72 @@ def test_empty_input_is_ok_without_launch():
     rs.rs_sort_keys_u32(None, None, 0, 0, 32, T, 1 << 20, stream=0)
     rs.rs_sort_pairs_u32(None, None, None, None, 0, 0, 32, T, 1 << 20, stream=0)
     rs.rs_bitonic_tile(None, None, 0, 16, 0, 32, stream=0)
+
+
+# --- typed keys, two-key sorts, digit counts ------------------------------------------
+
+def test_typed_key_checks():
+    for bad_type in (-1, 6, 99):
+        with pytest.raises(rs.RsError) as ei:
+            rs.rs_sort_keys(bad_type, 0, None, None, 16, 0, 32, None, 0)
+        assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    for kt in (rs.RS_KEY_U32, rs.RS_KEY_I32, rs.RS_KEY_F32):
+        assert rs.rs_sort_keys(kt, 1, None, None, 1000, 0, 32, None, 0) > 0
+        with pytest.raises(rs.RsError) as ei:
+            rs.rs_sort_pairs(kt, 0, None, None, None, None, 1000, 0, 33, None, 0)
+        assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    for kt in (rs.RS_KEY_U64, rs.RS_KEY_I64, rs.RS_KEY_F64):
+        assert rs.rs_sort_pairs(kt, 0, None, None, None, None, 1000, 0, 64, None, 0) > 0
+        with pytest.raises(rs.RsError) as ei:
+            rs.rs_sort_keys(kt, 0, None, None, 1000, 0, 65, None, 0)
+        assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+        with pytest.raises(rs.RsError) as ei:
+            rs.rs_sort_keys(kt, 0, None, None, 1 << 29, 0, 64, None, 0)
+        assert ei.value.status == rs.RS_ERR_UNSUPPORTED_SIZE
+        assert rs.rs_sort_keys(kt, 0, None, None, (1 << 29) - 1, 0, 64, None, 0) > 8 * ((1 << 29) - 1)
+
+
+def test_typed_temp_query_depends_only_on_n_and_width():
+    n = 1 << 20
+    u32 = rs.rs_sort_pairs(rs.RS_KEY_U32, 0, None, None, None, None, n, 0, 32, None, 0)
+    assert u32 == rs.rs_sort_pairs_u32(None, None, None, None, n, 0, 32, None, 0)
+    assert u32 == rs.rs_sort_pairs(rs.RS_KEY_F32, 1, None, None, None, None, n, 3, 9, None, 0)
+    u64 = rs.rs_sort_pairs(rs.RS_KEY_U64, 0, None, None, None, None, n, 0, 64, None, 0)
+    assert u64 == rs.rs_sort_pairs(rs.RS_KEY_F64, 1, None, None, None, None, n, 7, 40, None, 0)
+    assert u64 > 8 * n + 4 * n
+    keys64 = rs.rs_sort_keys(rs.RS_KEY_I64, 0, None, None, n, 0, 64, None, 0)
+    assert 8 * n < keys64 < u64
+
+
+def test_two_key_checks():
+    q = rs.rs_sort_two_keys_u32(None, None, None, None, None, None, 1 << 20, None, 0)
+    assert q > 2 * 8 * (1 << 20)   # two 8-byte key buffers in temp
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_sort_two_keys_u32(None, None, None, None, None, None, 1 << 29, None, 0)
+    assert ei.value.status == rs.RS_ERR_UNSUPPORTED_SIZE
+    with pytest.raises(rs.RsError) as ei:   # values in without values out
+        rs.rs_sort_two_keys_u32(A, B, C, D, T, None, 64, T + (1 << 24), 1 << 24, stream=0)
+    assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    with pytest.raises(rs.RsError) as ei:   # major out overlaps minor in
+        rs.rs_sort_two_keys_u32(A, B, B + 64, D, None, None, 64, T, 1 << 24, stream=0)
+    assert ei.value.status == rs.RS_ERR_OVERLAP
+
+
+def test_digit_count_checks():
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_digit_counts(rs.RS_KEY_U32, 0, A, 64, 0, 32, C + 2, stream=0)
+    assert ei.value.status == rs.RS_ERR_MISALIGNED
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_digit_counts(rs.RS_KEY_U32, 0, A + 4, 64, 0, 32, C, stream=0)
+    assert ei.value.status == rs.RS_ERR_MISALIGNED
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_digit_counts(rs.RS_KEY_U64, 0, A, 64, 0, 65, C, stream=0)
+    assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_digit_counts(rs.RS_KEY_U32, 0, A, 64, 0, 32, None, stream=0)
+    assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    with pytest.raises(rs.RsError) as ei:   # counts inside the keys
+        rs.rs_digit_counts(rs.RS_KEY_U32, 0, A, 1 << 20, 0, 32, A + 1024, stream=0)
+    assert ei.value.status == rs.RS_ERR_OVERLAP
+    # an empty bit range counts nothing and launches nothing
+    rs.rs_digit_counts(rs.RS_KEY_U32, 0, A, 64, 9, 9, C, stream=0)
