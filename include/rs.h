@@ -180,7 +180,8 @@ rs_status rs_sort_pairs(rs_key_type key_type, int descending, const void *keys_i
  * equals a stable sort by the minor key followed by a stable sort by the
  * major key.  major_in/minor_in [n] read only, major_out/minor_out [n]
  * written; vals_in/vals_out [n] u32, or both NULL for keys only.  n < 2^29.
- * Temp, streams and errors as for rs_sort_keys_u32.
+ * The temp size (query with d_temp == NULL) depends only on n and always
+ * allows for values.  Temp, streams and errors as for rs_sort_keys_u32.
  */
 rs_status rs_sort_two_keys_u32(const uint32_t *major_in, const uint32_t *minor_in,
                                uint32_t *major_out, uint32_t *minor_out, const uint32_t *vals_in,

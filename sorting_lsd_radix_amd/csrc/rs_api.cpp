@@ -108,7 +108,9 @@ rs_status sort_common(int key_type, bool descending, bool soa, const void* keys_
     const int key_bits = kind.key64 ? 64 : 32;
     if (begin_bit < 0 || end_bit > key_bits || begin_bit > end_bit) return RS_ERR_INVALID_VALUE;
     if (n >= (kind.key64 ? RS_MAX_N64 : RS_MAX_N)) return RS_ERR_UNSUPPORTED_SIZE;
-    const size_t need = sort_temp_bytes(n, pairs, kind);
+    // a two-key sort's values are optional, so its size query (made without
+    // pointers) always counts them
+    const size_t need = sort_temp_bytes(n, pairs || soa, kind);
     if (d_temp == nullptr) {
         *temp_bytes = need;
         return RS_OK;
