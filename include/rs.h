@@ -11,6 +11,7 @@
  *   rs_sort_two_keys_u32    stable sort by (major, minor) u32 key pairs
  *   rs_digit_counts         every 8-bit pass's digit counts of typed keys
  *   rs_compact_positive_f32 keep x > 0 in order, zero-fill the rest, count
+ *   rs_compact_positive_f32_noalloc  the same with static scratch (no temp)
  *   rs_bitonic_tile         sort each run of at most 1024 keys in LDS
  *   rs_status_string        text of a status code
  *
@@ -213,6 +214,23 @@ rs_status rs_digit_counts(rs_key_type key_type, int descending, const void *keys
  */
 rs_status rs_compact_positive_f32(const float *in, float *out, uint32_t *d_count, uint64_t n,
                                   void *d_temp, size_t *temp_bytes, hipStream_t stream);
+
+/*
+ * rs_compact_positive_f32 without a temp buffer, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid hipMalloc).  It runs the same kernels with the
+ * library's static scratch: a file-scope device array of 131,328 bytes (the
+ * tile counters and one state word per 32768-element tile for every n <
+ * 2^30), which each device the library runs on holds until the process ends.
+ * It calls no allocating routine.  n >= 2^30 returns RS_ERR_UNSUPPORTED_SIZE.
+ * The first call on a device looks up that device's copy of the array.
+ * Every call on one device shares its scratch, clearing it on the stream
+ * before use: calls that overlap on one device (different streams or host
+ * threads without ordering between them) race and give wrong results.
+ * Other arguments, results and errors as for rs_compact_positive_f32.
+ */
+rs_status rs_compact_positive_f32_noalloc(const float *in, float *out, uint32_t *d_count, uint64_t n,
+                                          hipStream_t stream);
 
 /*
  * Each run keys[s .. min(s + tile, n)), s = 0, tile, 2 tile, ..., is sorted

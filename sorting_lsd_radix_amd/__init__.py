@@ -22,7 +22,7 @@ __all__ = [
     "RS_KEY_U32", "RS_KEY_I32", "RS_KEY_F32", "RS_KEY_U64", "RS_KEY_I64", "RS_KEY_F64",
     "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_sort_keys", "rs_sort_pairs",
     "rs_sort_two_keys_u32", "rs_digit_counts", "rs_compact_positive_f32",
-    "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
+    "rs_compact_positive_f32_noalloc", "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
     "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "sort_keys", "sort_pairs",
     "sort_two_keys_u32", "digit_counts", "compact_positive_f32", "bitonic_tile",
     "library_path", "use_library", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
@@ -59,7 +59,8 @@ KERNEL_NAMES = {0: "upsweep", 1: "onesweep", 2: "sort_init", 3: "compact_init",
 
 EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32",
                     "rs_sort_keys", "rs_sort_pairs", "rs_sort_two_keys_u32", "rs_digit_counts",
-                    "rs_compact_positive_f32", "rs_bitonic_tile", "rs_status_string",
+                    "rs_compact_positive_f32", "rs_compact_positive_f32_noalloc",
+                    "rs_bitonic_tile", "rs_status_string",
                     "rs_timing_enable", "rs_timing_collect"]
 
 _lib = None
@@ -105,6 +106,8 @@ def _load():
     lib.rs_sort_two_keys_u32.argtypes = [vp, vp, vp, vp, vp, vp, u64, vp, szp, vp]
     lib.rs_digit_counts.argtypes = [i32, i32, vp, u64, i32, i32, vp, vp]
     lib.rs_compact_positive_f32.argtypes = [vp, vp, vp, u64, vp, szp, vp]
+    lib.rs_compact_positive_f32_noalloc.argtypes = [vp, vp, vp, u64, vp]
+    lib.rs_compact_positive_f32_noalloc.restype = i32
     lib.rs_bitonic_tile.argtypes = [vp, vp, u64, u32, i32, i32, vp]
     for f in (lib.rs_sort_keys_u32, lib.rs_sort_pairs_u32, lib.rs_sort_pairs_f32, lib.rs_sort_keys,
               lib.rs_sort_pairs, lib.rs_sort_two_keys_u32, lib.rs_digit_counts,
@@ -230,6 +233,13 @@ def rs_compact_positive_f32(x_in, x_out, d_count, n, d_temp, temp_bytes, stream=
                                          _stream(stream) if d_temp is not None else None)
     _call("rs_compact_positive_f32", st)
     return size.value if d_temp is None else None
+
+
+def rs_compact_positive_f32_noalloc(x_in, x_out, d_count, n, stream=None):
+    """C: rs_compact_positive_f32_noalloc (the library's static scratch, no temp)."""
+    st = _load().rs_compact_positive_f32_noalloc(_ptr(x_in), _ptr(x_out), _ptr(d_count), int(n),
+                                                 _stream(stream))
+    _call("rs_compact_positive_f32_noalloc", st)
 
 
 def rs_bitonic_tile(keys_in, keys_out, n, tile, begin_bit, end_bit, stream=None):

@@ -23,6 +23,8 @@
 //  * wave 0 looks back over 64 earlier tiles per step (agent-scope loads);
 //  * persistent blocks take tiles from the XCD-chunked scheduler, so the
 //    output runs of neighbouring tiles meet in one XCD's L2.
+#include <mutex>
+
 #include "device_common.hpp"
 #include "internal.hpp"
 
@@ -207,9 +209,47 @@ uint32_t compact_resident() {
     return resident;
 }
 
+// ---- allocation-free variant -----------------------------------------------------
+// The scratch of rs_compact_positive_f32_noalloc: a file-scope device array
+// big enough for the tile counters and tile states of every accepted size
+// (n < 2^30: 32768 tiles of 32768 elements).  Each device holds its own copy
+// until the process ends; in host code `scratch` only names the symbol, so
+// its device address is looked up once per device and kept.
+constexpr size_t kStaticScratchBytes = 256 + (static_cast<size_t>(RS_MAX_N / kCompTile) * 4 + 255) / 256 * 256;
+__device__ __align__(256) uint32_t scratch[kStaticScratchBytes / 4];
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of `scratch` on the current device (nullptr on failure).
+void* static_scratch() {
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) return nullptr;
+    std::lock_guard<std::mutex> lock(g_scratch_mutex);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        if (hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch)) != hipSuccess) return nullptr;
+        g_scratch_ptr[dev] = ptr;
+    }
+    return g_scratch_ptr[dev];
+}
+
 }  // namespace
 
 size_t compact_temp_bytes(uint64_t n) { return compact_layout(n).total; }
+
+size_t compact_static_scratch_bytes() { return kStaticScratchBytes; }
+
+hipError_t launch_compact_static(const float* in, float* out, uint32_t* d_count, uint32_t n,
+                                 hipStream_t stream) {
+    if (compact_layout(n).total > kStaticScratchBytes) return hipErrorInvalidValue;
+    void* ptr = static_scratch();
+    if (ptr == nullptr) return hipErrorInvalidSymbol;
+    // the same kernels as launch_compact; the fill kernel clears the counters
+    // and states the previous call left in the scratch
+    return launch_compact(in, out, d_count, n, ptr, stream);
+}
 
 hipError_t launch_compact(const float* in, float* out, uint32_t* d_count, uint32_t n, void* temp,
                           hipStream_t stream) {

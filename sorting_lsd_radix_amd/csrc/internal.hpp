@@ -77,6 +77,11 @@ hipError_t launch_fill_zero(uint32_t* p, uint64_t words, hipStream_t stream, int
 size_t compact_temp_bytes(uint64_t n);
 hipError_t launch_compact(const float* in, float* out, uint32_t* d_count, uint32_t n, void* temp,
                           hipStream_t stream);
+// The same compaction with the library's static per-device scratch instead of
+// a temp buffer (no allocation); fails if n needs more than that scratch.
+size_t compact_static_scratch_bytes();
+hipError_t launch_compact_static(const float* in, float* out, uint32_t* d_count, uint32_t n,
+                                 hipStream_t stream);
 
 // ---- bitonic tile -------------------------------------------------------------
 

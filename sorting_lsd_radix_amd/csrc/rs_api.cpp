@@ -278,6 +278,25 @@ rs_status rs_compact_positive_f32(const float* in, float* out, uint32_t* d_count
     return e == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 
+rs_status rs_compact_positive_f32_noalloc(const float* in, float* out, uint32_t* d_count,
+                                          uint64_t n, hipStream_t stream) {
+    using namespace rs;
+    if (n >= RS_MAX_N || compact_temp_bytes(n) > compact_static_scratch_bytes())
+        return RS_ERR_UNSUPPORTED_SIZE;
+    if (d_count == nullptr) return RS_ERR_INVALID_VALUE;
+    if (n > 0 && (in == nullptr || out == nullptr)) return RS_ERR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(d_count) & 3u) != 0) return RS_ERR_MISALIGNED;
+    if (n > 0 && (!aligned16(in) || !aligned16(out))) return RS_ERR_MISALIGNED;
+    if (n > 0 && overlaps({range_of(d_count, 4), range_of(in, n * 4), range_of(out, n * 4)}))
+        return RS_ERR_OVERLAP;
+    hipError_t e;
+    if (n == 0)
+        e = launch_fill_zero(d_count, 1, stream, RS_KERNEL_COMPACT_INIT);
+    else
+        e = launch_compact_static(in, out, d_count, static_cast<uint32_t>(n), stream);
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
 rs_status rs_bitonic_tile(const uint32_t* keys_in, uint32_t* keys_out, uint64_t n, uint32_t tile,
                           int begin_bit, int end_bit, hipStream_t stream) {
     using namespace rs;
