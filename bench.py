@@ -11,7 +11,8 @@ inputs, outputs and temp already resident in HBM.  Prints one JSON line.
 
 The roofline entry is for the dominant kernel of the workload (the one-sweep
 pass for sorts, the one-workgroup tile sort for sorts of at most 16384 keys,
-the compaction kernel for compaction): its algorithmic bytes per launch over
+the bucket sort for hybrid sorts of at most 3 * 2^20 keys, the compaction
+kernel for compaction): its algorithmic bytes per launch over
 its mean duration, timed with HIP events that the library
 records around each of its launches on the call's stream during the last
 twentieth (at least one) of the timed steps, inside the same timed region
@@ -36,6 +37,7 @@ sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBS = 8000.0
 TILE_SORT_MAX = 16384  # sorts up to this size run in one workgroup (one launch)
+HYBRID_MAX = 3 << 20   # up to this size a sort is one top-digit pass + one LDS sort per bucket
 PROFILES = os.path.join(ROOT, "profiles")
 TRAFFIC_FILE = os.path.join(PROFILES, "traffic.json")
 CSRC = os.path.join(ROOT, "sorting_lsd_radix_amd", "csrc")
@@ -300,6 +302,12 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         dom = "tile_sort"
         bytes_per = 8 if kind == "keys_u32" else 16
         algo_total = bytes_per * n
+    elif n <= HYBRID_MAX and passes >= 2:
+        # hybrid: the bucket sort (one read and one write of every key and value)
+        # after the top digit's pass; the metric still counts every pass's bytes
+        dom = "bucket_sort"
+        bytes_per = 8 if kind == "keys_u32" else 16
+        algo_total = bytes_per * n * passes
     else:
         dom = "onesweep"
         bytes_per = 8 if kind == "keys_u32" else 16
@@ -358,6 +366,7 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
 
 KERNEL_MATCH = {"onesweep": "onesweep_kernel", "upsweep": "upsweep_kernel",
                 "compact": "compact_kernel", "tile_sort": "tile_sort_kernel",
+                "bucket_sort": "bucket_sort_kernel",
                 "bitonic": "bitonic_tile_kernel", "copy": "__amd_rocclr_copyBuffer"}
 COPY_BYTES = 4 << 28   # the --copy-calibration copy moves 1 GiB each way
 
@@ -381,7 +390,8 @@ def record_traffic(name, fetch_dir, write_dir):
     fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
     desc, kind, n, b, e = WORKLOADS[name]
     dom = ("compact" if kind == "compact" else "bitonic" if kind == "bitonic"
-           else "tile_sort" if n <= TILE_SORT_MAX else "onesweep")
+           else "tile_sort" if n <= TILE_SORT_MAX
+           else "bucket_sort" if n <= HYBRID_MAX and (e - b) > 8 else "onesweep")
     bytes_per = 8 if kind in ("keys_u32", "compact", "bitonic") else 16
     f_factor = COPY_BYTES / (fetch["copy"] * 1024)
     w_factor = COPY_BYTES / (write["copy"] * 1024)

@@ -267,7 +267,8 @@ typedef enum rs_kernel_id {
     RS_KERNEL_COMPACT = 4,      /* single-pass compaction */
     RS_KERNEL_BITONIC = 5,      /* LDS bitonic tiles */
     RS_KERNEL_COPY = 6,         /* device copy for an empty bit range */
-    RS_KERNEL_TILE_SORT = 7     /* whole sort of n <= 16384 keys in one block */
+    RS_KERNEL_TILE_SORT = 7,    /* whole sort of n <= 16384 keys in one block */
+    RS_KERNEL_BUCKET_SORT = 8   /* hybrid sort: each top-digit bucket sorted in LDS */
 } rs_kernel_id;
 
 rs_status rs_timing_enable(int enable);

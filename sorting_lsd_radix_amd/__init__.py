@@ -22,7 +22,8 @@ __all__ = [
     "RS_KEY_U32", "RS_KEY_I32", "RS_KEY_F32", "RS_KEY_U64", "RS_KEY_I64", "RS_KEY_F64",
     "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_sort_keys", "rs_sort_pairs",
     "rs_sort_two_keys_u32", "rs_digit_counts", "rs_compact_positive_f32",
-    "rs_compact_positive_f32_noalloc", "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
+    "rs_compact_positive_f32_noalloc", "rs_bitonic_tile", "rs_status_string", "rs_timing_enable",
+    "rs_timing_collect",
     "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "sort_keys", "sort_pairs",
     "sort_two_keys_u32", "digit_counts", "compact_positive_f32", "bitonic_tile",
     "library_path", "use_library", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
@@ -54,8 +55,9 @@ RS_KERNEL_COMPACT = 4
 RS_KERNEL_BITONIC = 5
 RS_KERNEL_COPY = 6
 RS_KERNEL_TILE_SORT = 7
+RS_KERNEL_BUCKET_SORT = 8
 KERNEL_NAMES = {0: "upsweep", 1: "onesweep", 2: "sort_init", 3: "compact_init",
-                4: "compact", 5: "bitonic", 6: "copy", 7: "tile_sort"}
+                4: "compact", 5: "bitonic", 6: "copy", 7: "tile_sort", 8: "bucket_sort"}
 
 EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32",
                     "rs_sort_keys", "rs_sort_pairs", "rs_sort_two_keys_u32", "rs_digit_counts",

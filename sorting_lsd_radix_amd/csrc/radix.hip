@@ -73,6 +73,13 @@ constexpr int kKeysHugeBlock = 1024;
 constexpr uint64_t kKeysHugeMinN = 1ull << 27;
 // Up to this many keys the whole sort runs in one block, in LDS.
 constexpr uint32_t kTileSortMax = 16384;
+// Hybrid sorts of up to kHybridMaxN 4-byte keys: one pass on the top digit
+// (MSD), then one workgroup per bucket sorts the lower digits in LDS, when
+// no bucket holds more than kBucketCap keys (otherwise the LSD passes run).
+constexpr uint32_t kHybridMaxN = 3u << 20;
+constexpr int kBucketBlock = 1024;
+constexpr int kBucketItems = 16;
+constexpr uint32_t kBucketCap = kBucketBlock * kBucketItems;
 // Earlier tiles read per look-back batch.  A wave waits for every word of a
 // batch that any of its lanes still needs, so small batches win: 2 measured
 // best for the 16384-key tiles (8 is 2-4 % slower), 1 for the 24576-key pair
@@ -315,6 +322,10 @@ struct PassArgs {
     uint32_t groups;           // block groups = min(8, grid)
     uint32_t chunk_log2;       // tiles per chunk = 2^chunk_log2 (at most the blocks per group)
     uint32_t atomic_limit_log2;   // atomic rank while no digit holds more than 2^-this of the keys
+    // Launch gate of the hybrid sort: 0 runs always; 1 runs only when no
+    // count of gate_bins[0..255] exceeds gate_cap, 2 only when one does.
+    uint32_t gate, gate_cap;
+    const uint32_t* gate_bins;
 };
 
 // Loads the ITEMS keys of this lane for `tile`: row j of wave w is the 64
@@ -402,6 +413,12 @@ void onesweep_kernel(PassArgs a) {
     const uint32_t n = a.n, shift = a.shift, width = a.width, tiles = a.tiles;
     const uint32_t last_digit = (1u << width) - 1u;
     const uint32_t group = blockIdx.x % a.groups;
+
+    if (a.gate != 0) {   // uniform: a gated launch of the hybrid sort
+        const uint32_t c = (tid < kRadix) ? a.gate_bins[tid] : 0u;
+        const bool oversize = __syncthreads_or(c > a.gate_cap);
+        if (oversize != (a.gate == 2)) return;
+    }
 
     // global digit count of this pass (thread d holds digit d)
     const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
@@ -800,6 +817,156 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
     }
 }
 
+// ---------------------------------------------------------------------------
+// Bucket sort of the hybrid path ("第10章 并行模式：排序", 10.5, the mixed
+// strategy: a radix pass on the high bits, then a sort of each bucket on
+// its own).  The top digit's pass has already placed every key (transformed)
+// in its bucket, stably; block b sorts bucket b by the lower digits in LDS
+// with the same passes as the one-workgroup sort and writes it to its final
+// place.  The bucket's c keys are spread over the 16 waves as rows = ceil(c /
+// 1024) rows of 64 per wave, in input order (wave, row, lane); rows past
+// that are not touched, and the pads of the last rows (key 0xFFFFFFFF) rank
+// after every real key and are never stored.  The launch does nothing when a
+// bucket holds more than cap keys (then the LSD passes run instead).
+// ---------------------------------------------------------------------------
+struct BucketArgs {
+    const uint32_t* keys;        // bucketed (transformed) keys
+    const uint32_t* vals;
+    uint32_t* keys_out;
+    uint32_t* vals_out;
+    const uint32_t* top_bins;    // key counts of the buckets
+    uint32_t cap;
+    PassDigits pd;               // the digits below the top one
+    KeyXform xout;               // inverse transform on the store (XF_OUT)
+};
+
+template <bool PAIRS, bool XF_OUT>
+__global__ __launch_bounds__(kBucketBlock) void bucket_sort_kernel(BucketArgs a) {
+    constexpr int BLOCK = kBucketBlock;
+    constexpr int ITEMS = kBucketItems;
+    constexpr int WAVES = BLOCK / kWave;
+    constexpr int TILE = BLOCK * ITEMS;
+    static_assert((TILE & (TILE - 1)) == 0, "positions are masked to the tile");
+
+    __shared__ uint32_t s_keys[TILE];
+    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    __shared__ uint32_t s_off[WAVES * kRadix];
+    __shared__ uint32_t s_wsum[kRadix / kWave];
+    __shared__ uint32_t s_start;
+
+    const uint32_t tid = threadIdx.x;
+    const uint32_t lane = tid & (kWave - 1);
+    const uint32_t wave = tid / kWave;
+    const uint32_t b = blockIdx.x;
+
+    const uint32_t cd = (tid < kRadix) ? a.top_bins[tid] : 0u;
+    if (__syncthreads_or(cd > a.cap)) return;   // uniform: the LSD passes sort this input
+    if (wave == 0) {
+        // keys in the buckets below b: lane l adds the counts of buckets 4l .. 4l+3
+        uint32_t below = 0;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const uint32_t d = lane * 4 + i;
+            if (d < b) below += a.top_bins[d];
+        }
+#pragma unroll
+        for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off, kWave);
+        if (lane == 0) s_start = below;
+    }
+    __syncthreads();
+    const uint32_t start = s_start;
+    const uint32_t c = a.top_bins[b];
+    if (c == 0) return;   // uniform
+    const uint32_t rows = (c + BLOCK - 1) / BLOCK;
+    const uint32_t first = wave * (kWave * rows) + lane;   // row j of this lane: first + 64 j
+
+    uint32_t k[ITEMS];
+    uint32_t v[PAIRS ? ITEMS : 1];
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        if (j < static_cast<int>(rows)) {
+            const uint32_t i = first + j * kWave;
+            if (i < c) {
+                k[j] = a.keys[start + i];
+                if constexpr (PAIRS) v[j] = a.vals[start + i];
+            } else {
+                k[j] = 0xFFFFFFFFu;
+                if constexpr (PAIRS) v[j] = 0u;
+            }
+        }
+    }
+
+    for (uint32_t p = 0; p < a.pd.passes; ++p) {
+        const uint32_t shift = a.pd.shift[p], width = a.pd.width[p];
+        for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
+        uint32_t pos[ITEMS];
+        uint32_t* my_count = s_off + wave * kRadix;
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            if (j < static_cast<int>(rows)) {
+                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+#ifdef RS_FORCE_BALLOT_RANK
+                pos[j] = ballot_rank(my_count, d, lane);
+#else
+                pos[j] = atomicAdd(&my_count[d], 1u);   // served in lane order
+#endif
+            }
+        }
+        __syncthreads();
+        uint32_t count = 0;
+        if (tid < kRadix) {
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) {
+                const uint32_t cw = s_off[w * kRadix + tid];
+                s_off[w * kRadix + tid] = count;
+                count += cw;
+            }
+            const uint32_t inc = wave_inclusive_sum(count);
+            if (lane == kWave - 1) s_wsum[wave] = inc;
+            count = inc - count;
+        }
+        __syncthreads();
+        if (tid < kRadix) {
+            uint32_t st = count;
+#pragma unroll
+            for (int w = 0; w < kRadix / kWave; ++w)
+                if (w < static_cast<int>(wave)) st += s_wsum[w];
+#pragma unroll
+            for (int w = 0; w < WAVES; ++w) s_off[w * kRadix + tid] += st;
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            if (j < static_cast<int>(rows)) {
+                const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
+                const uint32_t q = (s_off[wave * kRadix + d] + pos[j]) & (TILE - 1);
+                s_keys[q] = k[j];
+                if constexpr (PAIRS) s_vals[q] = v[j];
+            }
+        }
+        __syncthreads();
+#pragma unroll
+        for (int j = 0; j < ITEMS; ++j) {
+            if (j < static_cast<int>(rows)) {
+                k[j] = s_keys[first + j * kWave];
+                if constexpr (PAIRS) v[j] = s_vals[first + j * kWave];
+            }
+        }
+        // the next pass writes the staging buffers only after two more barriers
+    }
+
+#pragma unroll
+    for (int j = 0; j < ITEMS; ++j) {
+        if (j < static_cast<int>(rows)) {
+            const uint32_t i = first + j * kWave;
+            if (i < c) {
+                a.keys_out[start + i] = XF_OUT ? xform32(k[j], a.xout) : k[j];
+                if constexpr (PAIRS) a.vals_out[start + i] = v[j];
+            }
+        }
+    }
+}
+
 // Temp layout (every piece 256-byte aligned):
 //   bins     [P][256]   u32   global digit counts of each pass (P = 4, or 8 for 64-bit keys)
 //   sched    [P][64]    u32   tile counters of each pass, one per group (next_chunked_tile)
@@ -1089,6 +1256,61 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
     e = launch_upsweep(io, kind, pd, bins, stream);
     if (e != hipSuccess) return e;
 
+    // Hybrid sort of a small input: the top digit's pass into temp, then one
+    // workgroup per bucket; both run only if no bucket of the top digit
+    // holds more than kBucketCap keys, and the LSD passes below only if one
+    // does (every launch reads the same counts, so exactly one path runs).
+    const int top = passes - 1;
+    const bool hybrid = !kind.key64 && passes >= 2 && n <= kHybridMaxN;
+    if (hybrid) {
+        PassArgs a{};
+        a.src_keys = io.keys_in;
+        a.src_vals = io.vals_in;
+        a.dst_keys = tmp_keys;
+        a.dst_vals = pairs ? tmp_vals : nullptr;
+        a.n = n;
+        a.tiles = L.tiles;
+        a.shift = pd.shift[top];
+        a.width = pd.width[top];
+        a.bins = bins + top * kRadix;
+        a.states = states[0];
+        a.next_states = nullptr;
+        a.sched = sched + static_cast<size_t>(top) * kSchedWords;
+        a.atomic_limit_log2 = 1u;   // input order, as a first pass
+        a.xin = kind.xf;
+        a.gate = 1u;
+        a.gate_cap = kBucketCap;
+        a.gate_bins = bins + top * kRadix;
+        timing_before(stream, RS_KERNEL_ONESWEEP);
+        e = pairs ? launch_pass<true>(kind.transforms, false, false, a, stream)
+                  : launch_pass<false>(kind.transforms, false, false, a, stream);
+        timing_after(stream);
+        if (e != hipSuccess) return e;
+
+        BucketArgs ba{};
+        ba.keys = tmp_keys;
+        ba.vals = pairs ? tmp_vals : nullptr;
+        ba.keys_out = io.keys_out;
+        ba.vals_out = io.vals_out;
+        ba.top_bins = bins + top * kRadix;
+        ba.cap = kBucketCap;
+        ba.pd = pd;
+        ba.pd.passes = static_cast<uint32_t>(top);
+        ba.xout = xout;
+        const dim3 grid(1u << pd.width[top]);
+        timing_before(stream, RS_KERNEL_BUCKET_SORT);
+        if (pairs) {
+            if (kind.transforms) bucket_sort_kernel<true, true><<<grid, kBucketBlock, 0, stream>>>(ba);
+            else bucket_sort_kernel<true, false><<<grid, kBucketBlock, 0, stream>>>(ba);
+        } else {
+            if (kind.transforms) bucket_sort_kernel<false, true><<<grid, kBucketBlock, 0, stream>>>(ba);
+            else bucket_sort_kernel<false, false><<<grid, kBucketBlock, 0, stream>>>(ba);
+        }
+        e = hipGetLastError();
+        timing_after(stream);
+        if (e != hipSuccess) return e;
+    }
+
     const uint32_t* sk = io.keys_in;
     const uint32_t* sv = io.vals_in;
     for (int p = 0; p < passes; ++p) {
@@ -1123,6 +1345,11 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
         a.atomic_limit_log2 = (p == 0) ? 1u : 4u;
         a.xin = kind.xf;
         a.xout = xout;
+        if (hybrid) {   // the fallback of the hybrid sort
+            a.gate = 2u;
+            a.gate_cap = kBucketCap;
+            a.gate_bins = bins + top * kRadix;
+        }
         const bool xf_in = kind.transforms && p == 0;
         const bool xf_out = kind.transforms && last;
         timing_before(stream, RS_KERNEL_ONESWEEP);
