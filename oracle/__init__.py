@@ -101,6 +101,11 @@ class Oracle:
         lib.oracle_digit_histograms_typed.restype = i32
         lib.oracle_sort_two_keys.argtypes = [_U32P, _U32P, _U32P, _U32P, _U32P, _U32P, u64]
         lib.oracle_sort_two_keys.restype = i32
+        lib.oracle_scan_u32.argtypes = [_U32P, _U32P, u64, i32]
+        lib.oracle_scan_u32.restype = None
+        lib.oracle_select.argtypes = [i32, i32, ctypes.c_uint32, _U32P, _U32P, _U32P, _U32P, u64,
+                                      i32]
+        lib.oracle_select.restype = ctypes.c_int64
         self.lib = lib
         self.path = path
 
@@ -284,6 +289,45 @@ class Oracle:
         return (f_out, s_out) if vals is None else (f_out, s_out, v_out)
 
 
+    # ---- scan and select -----------------------------------------------------------
+
+    def scan_u32(self, x, inclusive=False):
+        """Prefix sums of a uint32 array modulo 2^32 (exclusive by default)."""
+        x = _u32(x)
+        out = np.empty_like(x)
+        self.lib.oracle_scan_u32(_ptr(x, ctypes.c_uint32), _ptr(out, ctypes.c_uint32), x.size,
+                                 int(bool(inclusive)))
+        return out
+
+    def select(self, x, op, threshold, vals=None, partition=False):
+        """Elements of a uint32/int32/float32 array with `x OP threshold` (OP in
+        OPS), in input order; with partition the rejected ones follow in input
+        order.  Returns (out, count) or (out, vals_out, count); without
+        partition only out[:count] is defined (the rest is zero here)."""
+        x = np.ascontiguousarray(x)
+        key_type = KEY_TYPES[x.dtype.type]
+        if key_type > 2:
+            raise TypeError("select takes 4-byte elements")
+        bits = x.view(np.uint32)
+        tbits = int(np.array([threshold], x.dtype).view(np.uint32)[0])
+        out = np.zeros(x.size, np.uint32)
+        v_out = None
+        if vals is not None:
+            vals = _u32(vals)
+            if vals.size != x.size:
+                raise ValueError("values differ in length")
+            v_out = np.zeros(x.size, np.uint32)
+        k = _check(self.lib.oracle_select(key_type, OPS[op], tbits, _ptr(bits, ctypes.c_uint32),
+                                          _ptr(vals, ctypes.c_uint32), _ptr(out, ctypes.c_uint32),
+                                          _ptr(v_out, ctypes.c_uint32), x.size,
+                                          int(bool(partition))), "oracle_select")
+        out = out.view(x.dtype)
+        return (out, int(k)) if vals is None else (out, v_out, int(k))
+
+
+# comparison operators of select (the library uses the same numbering)
+OPS = {"<": 0, "<=": 1, ">": 2, ">=": 3, "==": 4, "!=": 5}
+
 # numpy scalar type -> key type code of oracle_sort_typed (the library uses
 # the same numbering)
 KEY_TYPES = {np.uint32: 0, np.int32: 1, np.float32: 2, np.uint64: 3, np.int64: 4, np.float64: 5}
@@ -341,3 +385,11 @@ def digit_histograms_typed(*a, **k):
 
 def sort_two_keys(*a, **k):
     return default().sort_two_keys(*a, **k)
+
+
+def scan_u32(*a, **k):
+    return default().scan_u32(*a, **k)
+
+
+def select(*a, **k):
+    return default().select(*a, **k)

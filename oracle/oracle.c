@@ -62,6 +62,20 @@
  *    key, then by the first, then by input position.
  *  - oracle_digit_histograms_typed: per-pass digit counts of the order
  *    patterns of any of the six key types (up to eight passes).
+ *  - oracle_scan_u32: the prefix sum the sort and the compaction are built
+ *    on ("CUDA 算子笔记 3", the scan methods of the Stream Compaction
+ *    section; "WebGPU Unleashed", 4.1: a digit pass as a prefix sum of digit
+ *    occurrences), exclusive or inclusive, in unsigned 32-bit arithmetic
+ *    (sums wrap modulo 2^32), by a plain running sum.
+ *  - oracle_select: the general form of the compaction ("CUDA 算子笔记 3",
+ *    Stream Compaction: predicate, scan, scatter): keep the elements whose
+ *    value satisfies `value OP threshold` (OP one of <, <=, >, >=, ==, !=,
+ *    compared as u32, i32 or f32 values with C semantics, so every
+ *    comparison with a NaN is false except !=), in input order, with
+ *    optional values moved alongside.  In partition mode the rejected
+ *    elements follow the kept ones, also in input order: the stable split
+ *    that one radix-sort pass per bit performs ("CUDA 算子笔记 3", Radix
+ *    Sort, the one-bit split).  Returns the kept count.
  *
  * Floating point: the compaction predicate is the C comparison x > 0.0f on
  * the float value, as the pages write it.  This file must be built without
@@ -585,4 +599,126 @@ int oracle_sort_two_keys(const uint32_t *first, const uint32_t *second, const ui
     }
     free(idx); free(perm1); free(tmp_keys); free(second_by1); free(perm);
     return rc;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Scan and select                                                           */
+/* ------------------------------------------------------------------------ */
+
+/* out[i] = in[0] + ... + in[i - 1] (exclusive) or + in[i] (inclusive), mod 2^32. */
+void oracle_scan_u32(const uint32_t *in, uint32_t *out, uint64_t n, int inclusive)
+{
+    uint32_t running = 0;
+    uint64_t i;
+    for (i = 0; i < n; ++i) {
+        uint32_t x = in[i];
+        if (inclusive) {
+            running += x;
+            out[i] = running;
+        } else {
+            out[i] = running;
+            running += x;
+        }
+    }
+}
+
+/* Comparison operators of oracle_select (the library uses the same numbering). */
+#define ORACLE_OP_LT 0
+#define ORACLE_OP_LE 1
+#define ORACLE_OP_GT 2
+#define ORACLE_OP_GE 3
+#define ORACLE_OP_EQ 4
+#define ORACLE_OP_NE 5
+
+static int compare_u32(uint32_t a, uint32_t b, int op)
+{
+    switch (op) {
+    case ORACLE_OP_LT: return a < b;
+    case ORACLE_OP_LE: return a <= b;
+    case ORACLE_OP_GT: return a > b;
+    case ORACLE_OP_GE: return a >= b;
+    case ORACLE_OP_EQ: return a == b;
+    default: return a != b;
+    }
+}
+
+static int compare_i32(int32_t a, int32_t b, int op)
+{
+    switch (op) {
+    case ORACLE_OP_LT: return a < b;
+    case ORACLE_OP_LE: return a <= b;
+    case ORACLE_OP_GT: return a > b;
+    case ORACLE_OP_GE: return a >= b;
+    case ORACLE_OP_EQ: return a == b;
+    default: return a != b;
+    }
+}
+
+static int compare_f32(float a, float b, int op)
+{
+    switch (op) {
+    case ORACLE_OP_LT: return a < b;
+    case ORACLE_OP_LE: return a <= b;
+    case ORACLE_OP_GT: return a > b;
+    case ORACLE_OP_GE: return a >= b;
+    case ORACLE_OP_EQ: return a == b;
+    default: return a != b;
+    }
+}
+
+/* Whether element i satisfies the predicate (key_type 0 = u32, 1 = i32, 2 = f32). */
+static int selected(int key_type, int op, uint32_t threshold_bits, const uint32_t *in, uint64_t i)
+{
+    uint32_t u = in[i];
+    if (key_type == ORACLE_KEY_U32)
+        return compare_u32(u, threshold_bits, op);
+    if (key_type == ORACLE_KEY_I32) {
+        int32_t a, b;
+        memcpy(&a, &u, 4);
+        memcpy(&b, &threshold_bits, 4);
+        return compare_i32(a, b, op);
+    } else {
+        float a, b;
+        memcpy(&a, &u, 4);
+        memcpy(&b, &threshold_bits, 4);
+        return compare_f32(a, b, op);
+    }
+}
+
+/*
+ * Keeps the elements of in[n] (4-byte u32, i32 or f32 values, given as bit
+ * patterns) with `value OP threshold`, in input order, at the front of out;
+ * vals (optional) move alongside into vals_out.  partition == 0: out[k..n)
+ * is left untouched; partition != 0: out[k..n) receives the rejected
+ * elements in input order.  Returns k, or a negative code.
+ */
+int64_t oracle_select(int key_type, int op, uint32_t threshold_bits, const uint32_t *in,
+                      const uint32_t *vals, uint32_t *out, uint32_t *vals_out, uint64_t n,
+                      int partition)
+{
+    uint64_t i, k = 0, r = 0;
+
+    if (key_type < ORACLE_KEY_U32 || key_type > ORACLE_KEY_F32 || op < 0 || op > ORACLE_OP_NE)
+        return ORACLE_BAD_ARGS;
+    if ((vals == NULL) != (vals_out == NULL))
+        return ORACLE_BAD_ARGS;
+    for (i = 0; i < n; ++i) {
+        if (selected(key_type, op, threshold_bits, in, i)) {
+            out[k] = in[i];
+            if (vals)
+                vals_out[k] = vals[i];
+            k += 1;
+        }
+    }
+    if (partition) {
+        for (i = 0; i < n; ++i) {
+            if (!selected(key_type, op, threshold_bits, in, i)) {
+                out[k + r] = in[i];
+                if (vals)
+                    vals_out[k + r] = vals[i];
+                r += 1;
+            }
+        }
+    }
+    return (int64_t)k;
 }

@@ -595,9 +595,90 @@ def pin_histograms_typed(o, n=1 << 15, seed=14):
     assert np.array_equal(h[0], by_range.astype(np.uint64))
 
 
+# --- scan and select --------------------------------------------------------------
+
+def pin_scan(o, seed=15):
+    """Prefix sums against numpy's cumsum (taken in 64 bits, then reduced
+    modulo 2^32) and closed forms."""
+    rng = np.random.default_rng(seed)
+    for n in (0, 1, 2, 63, 64, 65, 1000, 1 << 16):
+        for hi in (3, 2**20, 2**32):
+            x = rng.integers(0, hi, n, dtype=np.uint64).astype(np.uint32)
+            inc = (np.cumsum(x.astype(np.uint64)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+            exc = np.concatenate([np.zeros(min(n, 1), np.uint32), inc[:-1]]) if n else inc
+            assert np.array_equal(o.scan_u32(x, inclusive=True), inc), (n, hi)
+            assert np.array_equal(o.scan_u32(x), exc), (n, hi)
+    n = 100000
+    assert np.array_equal(o.scan_u32(np.ones(n, np.uint32)), np.arange(n, dtype=np.uint32))
+    i = np.arange(n, dtype=np.uint64)
+    tri = ((i * (i - 1) // 2) & np.uint64(0xFFFFFFFF)).astype(np.uint32)   # sum of 0 .. i-1
+    assert np.array_equal(o.scan_u32(np.arange(n, dtype=np.uint32)), tri)
+
+
+SELECT_OPS = ["<", "<=", ">", ">=", "==", "!="]
+
+
+def _np_compare(x, op, t):
+    return {"<": x < t, "<=": x <= t, ">": x > t, ">=": x >= t, "==": x == t, "!=": x != t}[op]
+
+
+def pin_select(o, seed=16):
+    """Select and partition against numpy boolean masks (IEEE comparisons for
+    floats, signed or unsigned for integers), the pages' worked compaction
+    example, and brute force with Python comparisons."""
+    g = read_golden("compaction_example.txt")
+    x = np.array([float(v) for v in g["in"]], np.float32)
+    kept, k = o.select(x, ">", 0.0)
+    assert k == int(g["count"][0])
+    want = np.array([float(v) for v in g["out"]], np.float32)[:k]
+    assert np.array_equal(kept[:k].view(np.uint32), want.view(np.uint32))
+    part, k = o.select(x, ">", 0.0, partition=True)
+    assert np.array_equal(part.view(np.uint32),
+                          np.concatenate([x[x > 0], x[~(x > 0)]]).view(np.uint32))
+    rng = np.random.default_rng(seed)
+    specials = np.array(FLOAT_LADDER, np.uint32).view(np.float32)
+    for dt in (np.uint32, np.int32, np.float32):
+        for n in (0, 1, 100, 4099, 70000):
+            if dt == np.float32:
+                x = random_float_patterns(rng, n).view(np.float32)
+                t_choices = list(specials) + [np.float32(0.5)]
+            else:
+                x = typed_sample(rng, dt, n)
+                t_choices = [dt(0), dt(7), np.array([0x80000000], np.uint32).view(dt)[0]]
+                if n:
+                    t_choices.append(x[n // 2])
+            vals = np.arange(n, dtype=np.uint32)
+            for op in SELECT_OPS:
+                t = t_choices[int(rng.integers(0, len(t_choices)))]
+                with np.errstate(invalid="ignore"):
+                    mask = _np_compare(x, op, t)
+                out, vo, k = o.select(x, op, t, vals)
+                assert k == int(mask.sum()), (dt, n, op, t)
+                raw = x.view(np.uint32)
+                assert np.array_equal(out.view(np.uint32)[:k], raw[mask]), (dt, n, op)
+                assert np.array_equal(vo[:k], vals[mask])
+                out, vo, k = o.select(x, op, t, vals, partition=True)
+                assert np.array_equal(out.view(np.uint32),
+                                      np.concatenate([raw[mask], raw[~mask]])), (dt, n, op)
+                assert np.array_equal(vo, np.concatenate([vals[mask], vals[~mask]]))
+    # brute force with Python comparisons on tiny inputs
+    ops = {"<": lambda a, b: a < b, "<=": lambda a, b: a <= b, ">": lambda a, b: a > b,
+           ">=": lambda a, b: a >= b, "==": lambda a, b: a == b, "!=": lambda a, b: a != b}
+    alphabet = [-1.5, -0.0, 0.0, 1e-40, 2.0, float("nan"), float("inf")]
+    for combo in itertools.product(alphabet, repeat=3):
+        x = np.array(combo, np.float32)
+        for op, f in ops.items():
+            for t in (0.0, 2.0, float("nan")):
+                keep = [i for i in range(3) if f(float(x[i]), t)]
+                out, k = o.select(x, op, t, partition=True)
+                order = keep + [i for i in range(3) if i not in keep]
+                assert k == len(keep) and np.array_equal(out.view(np.uint32),
+                                                         x.view(np.uint32)[order]), (combo, op, t)
+
+
 QUICK_PINS = [pin_radix_golden, pin_compaction_golden, pin_bitonic_golden,
               pin_bruteforce_exhaustive, pin_bruteforce_random, pin_float_order,
               pin_float_transform_sampled, pin_invariants_large, pin_digit_width_invariance,
               pin_special_cases, pin_histograms, pin_compaction, pin_bitonic_tile,
               pin_typed_bruteforce, pin_typed_bit_ranges, pin_u64_lsd, pin_two_keys,
-              pin_histograms_typed]
+              pin_histograms_typed, pin_scan, pin_select]

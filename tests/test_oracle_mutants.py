@@ -90,6 +90,18 @@ MUTANTS = [
     ("two-key sort: second step forgets the first step's order",
      "rc = oracle_lsd_sort_u32(second_by1, perm1, tmp_keys, perm, n, 0, 32, 8);",
      "rc = oracle_lsd_sort_u32(second, idx, tmp_keys, perm, n, 0, 32, 8);"),
+    ("exclusive scan adds the element first",
+     "out[i] = running;\n            running += x;", "running += x;\n            out[i] = running;"),
+    ("scan sums in the wrong direction",
+     "            running += x;\n            out[i] = running;", "            running -= x;\n            out[i] = running;"),
+    ("signed select compares as unsigned",
+     "return compare_i32(a, b, op);", "return compare_u32((uint32_t)a, (uint32_t)b, op);"),
+    ("float select compares bit patterns",
+     "return compare_f32(a, b, op);", "return compare_u32(u, threshold_bits, op);"),
+    ("partition puts the rejected elements in reverse order",
+     "for (i = 0; i < n; ++i) {\n            if (!selected(", "for (i = n; i-- > 0;) {\n            if (!selected("),
+    ("partition leaves the values of rejected elements behind",
+     "vals_out[k + r] = vals[i];", "vals_out[k + r] = vals[k + r];"),
     ("typed histogram ignores descending order",
      "uint64_t pat = order_pattern(key_type, descending, keys, i);",
      "uint64_t pat = order_pattern(key_type, 0, keys, i);"),
