@@ -41,6 +41,35 @@ __device__ __forceinline__ uint32_t keep_positive(uint32_t u) {
     return (u - 1u) < 0x7F800000u ? 1u : 0u;
 }
 
+// Writes out[first .. first + count): the values s_src[0 .. count) (or zeros
+// when s_src is null), with 4-byte stores up to the first 16-byte boundary,
+// 16-byte stores after it (thread t writes quad t, t + 1024, ...) and 4-byte
+// stores for the last count mod 4 elements.  `out` is 16-byte aligned.
+__device__ __forceinline__ void store_run(const uint32_t* s_src, __amdgpu_buffer_rsrc_t out,
+                                          uint32_t first, uint32_t count, uint32_t tid) {
+    uint32_t head = (4u - (first & 3u)) & 3u;
+    if (head > count) head = count;
+    const uint32_t quads = (count - head) / 4u;
+    const uint32_t tail = head + quads * 4u;
+    if (tid < head)
+        __builtin_amdgcn_raw_buffer_store_b32(s_src ? s_src[tid] : 0u, out,
+                                              static_cast<int>((first + tid) * 4u), 0, 0);
+    for (uint32_t q = tid; q < quads; q += kCompBlock) {
+        const uint32_t i = head + 4u * q;
+        u32x4 v = {0u, 0u, 0u, 0u};
+        if (s_src) {
+            v.x = s_src[i];
+            v.y = s_src[i + 1];
+            v.z = s_src[i + 2];
+            v.w = s_src[i + 3];
+        }
+        __builtin_amdgcn_raw_buffer_store_b128(v, out, static_cast<int>((first + i) * 4u), 0, 0);
+    }
+    if (tid < count - tail)
+        __builtin_amdgcn_raw_buffer_store_b32(s_src ? s_src[tail + tid] : 0u, out,
+                                              static_cast<int>((first + tail + tid) * 4u), 0, 0);
+}
+
 // Persistent: each block loops over the tiles the chunked scheduler hands it.
 __global__ __launch_bounds__(kCompBlock) void compact_kernel(const uint32_t* __restrict__ in,
                                                              uint32_t* __restrict__ out,
@@ -171,13 +200,11 @@ __global__ __launch_bounds__(kCompBlock) void compact_kernel(const uint32_t* __r
 
         // ---- contiguous stores: kept run, then this tile's share of the zero tail --
         const uint32_t excl = s_excl;
-        for (uint32_t i = tid; i < tile_count; i += kCompBlock)
-            __builtin_amdgcn_raw_buffer_store_b32(s_out[i], out_rsrc, static_cast<int>((excl + i) * 4u), 0, 0);
+        store_run(s_out, out_rsrc, excl, tile_count, tid);
         const uint32_t rejected_before = tile_base - excl;
         const uint32_t rejected = valid - tile_count;
         const uint32_t zero_first = n - rejected_before - rejected;
-        for (uint32_t i = tid; i < rejected; i += kCompBlock)
-            __builtin_amdgcn_raw_buffer_store_b32(0u, out_rsrc, static_cast<int>((zero_first + i) * 4u), 0, 0);
+        store_run(nullptr, out_rsrc, zero_first, rejected, tid);
         if (tid == 0 && tile == tiles - 1) *d_count = excl + tile_count;
     }
 }
