@@ -10,6 +10,10 @@
  *   rs_sort_pairs           ascending or descending, with or without values
  *   rs_sort_two_keys_u32    stable sort by (major, minor) u32 key pairs
  *   rs_digit_counts         every 8-bit pass's digit counts of typed keys
+ *   rs_exclusive_scan_u32   prefix sums (exclusive / inclusive), mod 2^32
+ *   rs_inclusive_scan_u32
+ *   rs_select               keep x OP threshold in order (u32/i32/f32, values)
+ *   rs_partition            kept in order, then rejected in order (stable split)
  *   rs_compact_positive_f32 keep x > 0 in order, zero-fill the rest, count
  *   rs_compact_positive_f32_noalloc  the same with static scratch (no temp)
  *   rs_bitonic_tile         sort each run of at most 1024 keys in LDS
@@ -204,6 +208,61 @@ rs_status rs_digit_counts(rs_key_type key_type, int descending, const void *keys
                           int begin_bit, int end_bit, uint32_t *d_counts, hipStream_t stream);
 
 /*
+ * Prefix sums of u32 elements in one pass over the data, by a decoupled
+ * look-back over per-tile sums ("CUDA 算子笔记 3", the scan methods of the
+ * Stream Compaction section: each element read and written once):
+ * exclusive out[i] = in[0] + ... + in[i-1], inclusive out[i] = in[0] + ... +
+ * in[i], both modulo 2^32.  in [n] read only, out [n] written (in == out is
+ * allowed: every tile reads its elements before any of its outputs are
+ * stored, and no tile reads another's elements).  n < 2^30.  Temp with the
+ * query idiom (d_temp == NULL writes the size).  Errors as for the sorts.
+ */
+rs_status rs_exclusive_scan_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *d_temp,
+                                size_t *temp_bytes, hipStream_t stream);
+rs_status rs_inclusive_scan_u32(const uint32_t *in, uint32_t *out, uint64_t n, void *d_temp,
+                                size_t *temp_bytes, hipStream_t stream);
+
+/* Comparison of rs_select / rs_partition: element OP threshold. */
+typedef enum rs_compare_op {
+    RS_OP_LT = 0,
+    RS_OP_LE = 1,
+    RS_OP_GT = 2,
+    RS_OP_GE = 3,
+    RS_OP_EQ = 4,
+    RS_OP_NE = 5
+} rs_compare_op;
+
+/*
+ * Select: out[0..k) = the elements x of in with `x OP threshold`, in input
+ * order, *d_count = k; out[k..n) is not written ("CUDA 算子笔记 3", Stream
+ * Compaction: predicate, scan of the predicate, scatter -- here with any
+ * comparison).  key_type: RS_KEY_U32, RS_KEY_I32 or RS_KEY_F32 (4-byte
+ * elements compared as unsigned, signed or IEEE float values; a NaN compares
+ * unequal to everything and fails every other comparison).
+ * threshold_bits: the bit pattern of the threshold in that type.
+ * vals_in/vals_out: optional u32 values moved with the kept elements (both
+ * NULL for none).  in [n] and vals_in read only.  d_count: one u32 in device
+ * memory.  n < 2^30.  Temp with the query idiom (the size depends on n and
+ * on whether values are given).  Errors as for rs_compact_positive_f32.
+ */
+rs_status rs_select(rs_key_type key_type, rs_compare_op op, uint32_t threshold_bits, const void *in,
+                    void *out, const uint32_t *vals_in, uint32_t *vals_out, uint32_t *d_count,
+                    uint64_t n, void *d_temp, size_t *temp_bytes, hipStream_t stream);
+
+/*
+ * Stable partition: out[0..k) = the elements with `x OP threshold` in input
+ * order, out[k..n) = the others in input order, *d_count = k (the one-bit
+ * split that a radix-sort pass performs per bit, "CUDA 算子笔记 3", Radix
+ * Sort).  A first launch counts the kept elements, so each tile can place its
+ * rejected run at k + the rejected elements of earlier tiles.  Arguments as
+ * for rs_select; every output element is written.
+ */
+rs_status rs_partition(rs_key_type key_type, rs_compare_op op, uint32_t threshold_bits,
+                       const void *in, void *out, const uint32_t *vals_in, uint32_t *vals_out,
+                       uint32_t *d_count, uint64_t n, void *d_temp, size_t *temp_bytes,
+                       hipStream_t stream);
+
+/*
  * Stream compaction: out[0..k) = the inputs with x > 0.0f in input order,
  * out[k..n) = +0.0f, *d_count = k ("CUDA 算子笔记 3", section Stream
  * Compaction and its decoupled look-back method).  The predicate is taken
@@ -268,7 +327,12 @@ typedef enum rs_kernel_id {
     RS_KERNEL_BITONIC = 5,      /* LDS bitonic tiles */
     RS_KERNEL_COPY = 6,         /* device copy for an empty bit range */
     RS_KERNEL_TILE_SORT = 7,    /* whole sort of n <= 16384 keys in one block */
-    RS_KERNEL_BUCKET_SORT = 8   /* hybrid sort: each top-digit bucket sorted in LDS */
+    RS_KERNEL_BUCKET_SORT = 8,  /* hybrid sort: each top-digit bucket sorted in LDS */
+    RS_KERNEL_SCAN_INIT = 9,    /* clears the scan's counters and states */
+    RS_KERNEL_SCAN = 10,        /* single-pass prefix sum */
+    RS_KERNEL_SELECT_INIT = 11, /* clears select/partition counters and states */
+    RS_KERNEL_SELECT_COUNT = 12,/* partition: kept elements of the whole input */
+    RS_KERNEL_SELECT = 13       /* single-pass select / partition */
 } rs_kernel_id;
 
 rs_status rs_timing_enable(int enable);

@@ -22,8 +22,10 @@ __all__ = [
     "RS_KEY_U32", "RS_KEY_I32", "RS_KEY_F32", "RS_KEY_U64", "RS_KEY_I64", "RS_KEY_F64",
     "rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32", "rs_sort_keys", "rs_sort_pairs",
     "rs_sort_two_keys_u32", "rs_digit_counts", "rs_compact_positive_f32",
-    "rs_compact_positive_f32_noalloc", "rs_bitonic_tile", "rs_status_string", "rs_timing_enable",
-    "rs_timing_collect",
+    "rs_compact_positive_f32_noalloc", "rs_exclusive_scan_u32", "rs_inclusive_scan_u32",
+    "rs_select", "rs_partition", "RS_OP_LT", "RS_OP_LE", "RS_OP_GT", "RS_OP_GE", "RS_OP_EQ",
+    "RS_OP_NE", "rs_bitonic_tile", "rs_status_string", "rs_timing_enable", "rs_timing_collect",
+    "exclusive_scan_u32", "inclusive_scan_u32", "select", "partition",
     "sort_keys_u32", "sort_pairs_u32", "sort_pairs_f32", "sort_keys", "sort_pairs",
     "sort_two_keys_u32", "digit_counts", "compact_positive_f32", "bitonic_tile",
     "library_path", "use_library", "EXPORTED_SYMBOLS", "KERNEL_NAMES",
@@ -57,11 +59,17 @@ RS_KERNEL_COPY = 6
 RS_KERNEL_TILE_SORT = 7
 RS_KERNEL_BUCKET_SORT = 8
 KERNEL_NAMES = {0: "upsweep", 1: "onesweep", 2: "sort_init", 3: "compact_init",
-                4: "compact", 5: "bitonic", 6: "copy", 7: "tile_sort", 8: "bucket_sort"}
+                4: "compact", 5: "bitonic", 6: "copy", 7: "tile_sort", 8: "bucket_sort",
+                9: "scan_init", 10: "scan", 11: "select_init", 12: "select_count", 13: "select"}
+
+RS_OP_LT, RS_OP_LE, RS_OP_GT, RS_OP_GE, RS_OP_EQ, RS_OP_NE = range(6)
+_OPS = {"<": RS_OP_LT, "<=": RS_OP_LE, ">": RS_OP_GT, ">=": RS_OP_GE, "==": RS_OP_EQ,
+        "!=": RS_OP_NE}
 
 EXPORTED_SYMBOLS = ["rs_sort_keys_u32", "rs_sort_pairs_u32", "rs_sort_pairs_f32",
                     "rs_sort_keys", "rs_sort_pairs", "rs_sort_two_keys_u32", "rs_digit_counts",
                     "rs_compact_positive_f32", "rs_compact_positive_f32_noalloc",
+                    "rs_exclusive_scan_u32", "rs_inclusive_scan_u32", "rs_select", "rs_partition",
                     "rs_bitonic_tile", "rs_status_string",
                     "rs_timing_enable", "rs_timing_collect"]
 
@@ -110,6 +118,12 @@ def _load():
     lib.rs_compact_positive_f32.argtypes = [vp, vp, vp, u64, vp, szp, vp]
     lib.rs_compact_positive_f32_noalloc.argtypes = [vp, vp, vp, u64, vp]
     lib.rs_compact_positive_f32_noalloc.restype = i32
+    for f in (lib.rs_exclusive_scan_u32, lib.rs_inclusive_scan_u32):
+        f.argtypes = [vp, vp, u64, vp, szp, vp]
+        f.restype = i32
+    for f in (lib.rs_select, lib.rs_partition):
+        f.argtypes = [i32, i32, u32, vp, vp, vp, vp, vp, u64, vp, szp, vp]
+        f.restype = i32
     lib.rs_bitonic_tile.argtypes = [vp, vp, u64, u32, i32, i32, vp]
     for f in (lib.rs_sort_keys_u32, lib.rs_sort_pairs_u32, lib.rs_sort_pairs_f32, lib.rs_sort_keys,
               lib.rs_sort_pairs, lib.rs_sort_two_keys_u32, lib.rs_digit_counts,
@@ -242,6 +256,50 @@ def rs_compact_positive_f32_noalloc(x_in, x_out, d_count, n, stream=None):
     st = _load().rs_compact_positive_f32_noalloc(_ptr(x_in), _ptr(x_out), _ptr(d_count), int(n),
                                                  _stream(stream))
     _call("rs_compact_positive_f32_noalloc", st)
+
+
+def _scan_call(fn, what, x_in, x_out, n, d_temp, temp_bytes, stream):
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = fn(_ptr(x_in), _ptr(x_out), int(n), _ptr(d_temp), ctypes.byref(size),
+            _stream(stream) if d_temp is not None else None)
+    _call(what, st)
+    return size.value if d_temp is None else None
+
+
+def rs_exclusive_scan_u32(x_in, x_out, n, d_temp, temp_bytes, stream=None):
+    """C: rs_exclusive_scan_u32.  With d_temp None, returns the temp size."""
+    return _scan_call(_load().rs_exclusive_scan_u32, "rs_exclusive_scan_u32", x_in, x_out, n,
+                      d_temp, temp_bytes, stream)
+
+
+def rs_inclusive_scan_u32(x_in, x_out, n, d_temp, temp_bytes, stream=None):
+    """C: rs_inclusive_scan_u32.  With d_temp None, returns the temp size."""
+    return _scan_call(_load().rs_inclusive_scan_u32, "rs_inclusive_scan_u32", x_in, x_out, n,
+                      d_temp, temp_bytes, stream)
+
+
+def _select_call(fn, what, key_type, op, threshold_bits, x_in, x_out, vals_in, vals_out, d_count,
+                 n, d_temp, temp_bytes, stream):
+    size = ctypes.c_size_t(0 if temp_bytes is None else int(temp_bytes))
+    st = fn(int(key_type), int(op), int(threshold_bits) & 0xFFFFFFFF, _ptr(x_in), _ptr(x_out),
+            _ptr(vals_in), _ptr(vals_out), _ptr(d_count), int(n), _ptr(d_temp), ctypes.byref(size),
+            _stream(stream) if d_temp is not None else None)
+    _call(what, st)
+    return size.value if d_temp is None else None
+
+
+def rs_select(key_type, op, threshold_bits, x_in, x_out, vals_in, vals_out, d_count, n, d_temp,
+              temp_bytes, stream=None):
+    """C: rs_select.  With d_temp None, returns the temp size."""
+    return _select_call(_load().rs_select, "rs_select", key_type, op, threshold_bits, x_in, x_out,
+                        vals_in, vals_out, d_count, n, d_temp, temp_bytes, stream)
+
+
+def rs_partition(key_type, op, threshold_bits, x_in, x_out, vals_in, vals_out, d_count, n, d_temp,
+                 temp_bytes, stream=None):
+    """C: rs_partition.  With d_temp None, returns the temp size."""
+    return _select_call(_load().rs_partition, "rs_partition", key_type, op, threshold_bits, x_in,
+                        x_out, vals_in, vals_out, d_count, n, d_temp, temp_bytes, stream)
 
 
 def rs_bitonic_tile(keys_in, keys_out, n, tile, begin_bit, end_bit, stream=None):
@@ -390,6 +448,61 @@ def digit_counts(keys, descending=False, begin_bit=0, end_bit=None, stream=None)
     counts = torch.zeros((max(passes, 1), 256), dtype=torch.uint32, device=keys.device)
     rs_digit_counts(kt, descending, keys, keys.numel(), begin_bit, end_bit, counts, stream)
     return counts[:passes]
+
+
+def _scan_tensor(fn, x, out, temp, stream):
+    import torch
+    _check_tensor(x, torch.uint32, "x")
+    out = torch.empty_like(x) if out is None else out
+    need = fn(None, None, x.numel(), None, 0)
+    temp = _temp(need, x.device) if temp is None else temp
+    fn(x, out, x.numel(), temp, temp.numel(), stream)
+    return out
+
+
+def exclusive_scan_u32(x, out=None, temp=None, stream=None):
+    """Exclusive prefix sums of a uint32 tensor, modulo 2^32."""
+    return _scan_tensor(rs_exclusive_scan_u32, x, out, temp, stream)
+
+
+def inclusive_scan_u32(x, out=None, temp=None, stream=None):
+    """Inclusive prefix sums of a uint32 tensor, modulo 2^32."""
+    return _scan_tensor(rs_inclusive_scan_u32, x, out, temp, stream)
+
+
+def _threshold_bits(x, threshold):
+    import numpy as np
+    dt = {RS_KEY_U32: np.uint32, RS_KEY_I32: np.int32, RS_KEY_F32: np.float32}
+    kt, _ = _key_type(x)
+    if kt not in dt:
+        raise TypeError("select and partition take uint32, int32 or float32 elements")
+    return kt, int(np.array([threshold], dt[kt]).view(np.uint32)[0])
+
+
+def _select_tensor(fn, x, op, threshold, vals, temp, stream):
+    import torch
+    kt, bits = _threshold_bits(x, threshold)
+    out = torch.empty_like(x)
+    vo = None
+    if vals is not None:
+        _check_tensor(vals, torch.uint32, "vals")
+        vo = torch.empty_like(vals)
+    count = torch.empty(1, dtype=torch.uint32, device=x.device)
+    need = fn(kt, _OPS[op], bits, None, None, vals, vo, None, x.numel(), None, 0)
+    temp = _temp(need, x.device) if temp is None else temp
+    fn(kt, _OPS[op], bits, x, out, vals, vo, count, x.numel(), temp, temp.numel(), stream)
+    return (out, count) if vals is None else (out, vo, count)
+
+
+def select(x, op, threshold, vals=None, temp=None, stream=None):
+    """Elements with `x op threshold` (op in <, <=, >, >=, ==, !=) in order at the front of
+    the output; returns (out, count) or (out, vals_out, count); count is a 1-element tensor."""
+    return _select_tensor(rs_select, x, op, threshold, vals, temp, stream)
+
+
+def partition(x, op, threshold, vals=None, temp=None, stream=None):
+    """Stable partition: kept elements in order, then the rest in order."""
+    return _select_tensor(rs_partition, x, op, threshold, vals, temp, stream)
 
 
 def compact_positive_f32(x, out=None, count=None, temp=None, stream=None):

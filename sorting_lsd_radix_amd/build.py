@@ -7,7 +7,7 @@ ROOT = os.path.dirname(PKG)
 CSRC = os.path.join(PKG, "csrc")
 INCLUDE = os.path.join(ROOT, "include")
 LIB_PATH = os.path.join(PKG, "librs.so")
-SOURCES = ["radix.hip", "compact.hip", "bitonic.hip", "rs_api.cpp"]
+SOURCES = ["radix.hip", "compact.hip", "scan.hip", "bitonic.hip", "rs_api.cpp"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 FLAGS = [

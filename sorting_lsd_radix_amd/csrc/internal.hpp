@@ -83,6 +83,17 @@ size_t compact_static_scratch_bytes();
 hipError_t launch_compact_static(const float* in, float* out, uint32_t* d_count, uint32_t n,
                                  hipStream_t stream);
 
+// ---- scan, select, partition ------------------------------------------------------
+
+size_t scan_temp_bytes(uint64_t n);
+hipError_t launch_scan(const uint32_t* in, uint32_t* out, uint32_t n, bool inclusive, void* temp,
+                       hipStream_t stream);
+size_t select_temp_bytes(uint64_t n, bool pairs);
+hipError_t launch_select(int key_type, int op, uint32_t threshold_bits, const uint32_t* in,
+                         uint32_t* out, const uint32_t* vals_in, uint32_t* vals_out,
+                         uint32_t* d_count, uint32_t n, bool partition, void* temp,
+                         hipStream_t stream);
+
 // ---- bitonic tile -------------------------------------------------------------
 
 hipError_t launch_bitonic(const uint32_t* keys_in, uint32_t* keys_out, uint32_t n, uint32_t tile,

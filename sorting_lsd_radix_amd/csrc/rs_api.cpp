@@ -278,6 +278,98 @@ rs_status rs_compact_positive_f32(const float* in, float* out, uint32_t* d_count
     return e == hipSuccess ? RS_OK : RS_ERR_HIP;
 }
 
+static rs_status scan_common(const uint32_t* in, uint32_t* out, uint64_t n, void* d_temp,
+                             size_t* temp_bytes, hipStream_t stream, bool inclusive) {
+    using namespace rs;
+    if (temp_bytes == nullptr) return RS_ERR_INVALID_VALUE;
+    if (n >= RS_MAX_N) return RS_ERR_UNSUPPORTED_SIZE;
+    const size_t need = scan_temp_bytes(n);
+    if (d_temp == nullptr) {
+        *temp_bytes = need;
+        return RS_OK;
+    }
+    if (n == 0) return RS_OK;
+    if (in == nullptr || out == nullptr) return RS_ERR_INVALID_VALUE;
+    if (!aligned16(in) || !aligned16(out) || !aligned16(d_temp)) return RS_ERR_MISALIGNED;
+    if (*temp_bytes < need) return RS_ERR_TEMP_TOO_SMALL;
+    // in and out may be the same array; neither may overlap the temp, nor
+    // each other partially
+    if (in != out && overlaps({range_of(in, n * 4), range_of(out, n * 4)})) return RS_ERR_OVERLAP;
+    if (overlaps({range_of(in, n * 4), range_of(d_temp, need)}) ||
+        overlaps({range_of(out, n * 4), range_of(d_temp, need)}))
+        return RS_ERR_OVERLAP;
+    const hipError_t e = launch_scan(in, out, static_cast<uint32_t>(n), inclusive, d_temp, stream);
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+rs_status rs_exclusive_scan_u32(const uint32_t* in, uint32_t* out, uint64_t n, void* d_temp,
+                                size_t* temp_bytes, hipStream_t stream) {
+    return scan_common(in, out, n, d_temp, temp_bytes, stream, false);
+}
+
+rs_status rs_inclusive_scan_u32(const uint32_t* in, uint32_t* out, uint64_t n, void* d_temp,
+                                size_t* temp_bytes, hipStream_t stream) {
+    return scan_common(in, out, n, d_temp, temp_bytes, stream, true);
+}
+
+static rs_status select_common(int key_type, int op, uint32_t threshold_bits, const void* in,
+                               void* out, const uint32_t* vals_in, uint32_t* vals_out,
+                               uint32_t* d_count, uint64_t n, void* d_temp, size_t* temp_bytes,
+                               hipStream_t stream, bool partition) {
+    using namespace rs;
+    if (temp_bytes == nullptr) return RS_ERR_INVALID_VALUE;
+    if (key_type != RS_KEY_U32 && key_type != RS_KEY_I32 && key_type != RS_KEY_F32)
+        return RS_ERR_INVALID_VALUE;
+    if (op < RS_OP_LT || op > RS_OP_NE) return RS_ERR_INVALID_VALUE;
+    if ((vals_in == nullptr) != (vals_out == nullptr)) return RS_ERR_INVALID_VALUE;
+    if (n >= RS_MAX_N) return RS_ERR_UNSUPPORTED_SIZE;
+    const bool pairs = vals_in != nullptr;
+    const size_t need = select_temp_bytes(n, pairs);
+    if (d_temp == nullptr) {
+        *temp_bytes = need;
+        return RS_OK;
+    }
+    if (d_count == nullptr) return RS_ERR_INVALID_VALUE;
+    if (n > 0 && (in == nullptr || out == nullptr)) return RS_ERR_INVALID_VALUE;
+    if ((reinterpret_cast<uintptr_t>(d_count) & 3u) != 0 || !aligned16(d_temp)) return RS_ERR_MISALIGNED;
+    if (n > 0 && (!aligned16(in) || !aligned16(out))) return RS_ERR_MISALIGNED;
+    if (pairs && n > 0 && (!aligned16(vals_in) || !aligned16(vals_out))) return RS_ERR_MISALIGNED;
+    if (*temp_bytes < need) return RS_ERR_TEMP_TOO_SMALL;
+    std::vector<Range> rs{range_of(d_count, 4), range_of(d_temp, need)};
+    if (n > 0) {
+        rs.push_back(range_of(in, n * 4));
+        rs.push_back(range_of(out, n * 4));
+        if (pairs) {
+            rs.push_back(range_of(vals_in, n * 4));
+            rs.push_back(range_of(vals_out, n * 4));
+        }
+    }
+    if (overlaps(rs)) return RS_ERR_OVERLAP;
+    hipError_t e;
+    if (n == 0)
+        e = launch_fill_zero(d_count, 1, stream, RS_KERNEL_SELECT_INIT);
+    else
+        e = launch_select(key_type, op, threshold_bits, static_cast<const uint32_t*>(in),
+                          static_cast<uint32_t*>(out), vals_in, vals_out, d_count,
+                          static_cast<uint32_t>(n), partition, d_temp, stream);
+    return e == hipSuccess ? RS_OK : RS_ERR_HIP;
+}
+
+rs_status rs_select(rs_key_type key_type, rs_compare_op op, uint32_t threshold_bits, const void* in,
+                    void* out, const uint32_t* vals_in, uint32_t* vals_out, uint32_t* d_count,
+                    uint64_t n, void* d_temp, size_t* temp_bytes, hipStream_t stream) {
+    return select_common(key_type, op, threshold_bits, in, out, vals_in, vals_out, d_count, n,
+                         d_temp, temp_bytes, stream, false);
+}
+
+rs_status rs_partition(rs_key_type key_type, rs_compare_op op, uint32_t threshold_bits,
+                       const void* in, void* out, const uint32_t* vals_in, uint32_t* vals_out,
+                       uint32_t* d_count, uint64_t n, void* d_temp, size_t* temp_bytes,
+                       hipStream_t stream) {
+    return select_common(key_type, op, threshold_bits, in, out, vals_in, vals_out, d_count, n,
+                         d_temp, temp_bytes, stream, true);
+}
+
 rs_status rs_compact_positive_f32_noalloc(const float* in, float* out, uint32_t* d_count,
                                           uint64_t n, hipStream_t stream) {
     using namespace rs;

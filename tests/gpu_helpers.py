@@ -157,3 +157,39 @@ def gpu_digit_counts(keys, descending=False, b=0, e=None):
     counts = poisoned(max(passes, 1) * 256)
     rs.rs_digit_counts(kt, descending, tk, keys.size, b, e, counts)
     return host(counts)[: passes * 256].reshape(passes, 256)
+
+
+def gpu_scan(x, inclusive=False, inplace=False):
+    """rs_exclusive_scan_u32 / rs_inclusive_scan_u32 through the C ABI."""
+    n = x.size
+    fn = rs.rs_inclusive_scan_u32 if inclusive else rs.rs_exclusive_scan_u32
+    tx = to_dev(x)
+    out = tx if inplace else poisoned(n)
+    need = fn(None, None, n, None, 0)
+    temp = temp_for(need)
+    fn(tx, out, n, temp, temp.numel())
+    o = host(out)
+    if not inplace:
+        assert np.array_equal(host(tx), x), "input modified"
+    return o
+
+
+def gpu_select(x, op, threshold, vals=None, partition=False):
+    """rs_select / rs_partition through the C ABI; returns (out, vals_out or None, count).
+    Without partition only out[:count] is defined (the rest keeps the poison)."""
+    n = x.size
+    kt = _KEY_TYPE[x.dtype.type]
+    bits = int(np.array([threshold], x.dtype).view(np.uint32)[0])
+    fn = rs.rs_partition if partition else rs.rs_select
+    tx = to_dev(x)
+    out = poisoned_like(x)
+    tv = to_dev(vals) if vals is not None else None
+    vo = poisoned(n) if vals is not None else None
+    cnt = poisoned(1)
+    need = fn(kt, rs._OPS[op], bits, None, None, tv, vo, None, n, None, 0)
+    temp = temp_for(need)
+    fn(kt, rs._OPS[op], bits, tx, out, tv, vo, cnt, n, temp, temp.numel())
+    o, c = host(out), int(host(cnt)[0])
+    v = host(vo) if vals is not None else None
+    assert np.array_equal(_raw(host(tx)), _raw(x)), "input modified"
+    return o, v, c

@@ -208,3 +208,31 @@ def test_digit_count_checks():
     assert ei.value.status == rs.RS_ERR_OVERLAP
     # an empty bit range counts nothing and launches nothing
     rs.rs_digit_counts(rs.RS_KEY_U32, 0, A, 64, 9, 9, C, stream=0)
+
+
+def test_scan_and_select_checks():
+    assert rs.rs_exclusive_scan_u32(None, None, 1 << 20, None, 0) > 0
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_inclusive_scan_u32(None, None, 1 << 30, None, 0)
+    assert ei.value.status == rs.RS_ERR_UNSUPPORTED_SIZE
+    with pytest.raises(rs.RsError) as ei:   # partial overlap of in and out
+        rs.rs_exclusive_scan_u32(A, A + 16, 64, T, 1 << 20, stream=0)
+    assert ei.value.status == rs.RS_ERR_OVERLAP
+    with pytest.raises(rs.RsError) as ei:
+        rs.rs_exclusive_scan_u32(A + 4, B, 64, T, 1 << 20, stream=0)
+    assert ei.value.status == rs.RS_ERR_MISALIGNED
+    for bad in [(rs.RS_KEY_U64, rs.RS_OP_GT), (rs.RS_KEY_F32, 6), (rs.RS_KEY_F32, -1)]:
+        with pytest.raises(rs.RsError) as ei:
+            rs.rs_select(bad[0], bad[1], 0, None, None, None, None, None, 64, None, 0)
+        assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    with pytest.raises(rs.RsError) as ei:   # values in without values out
+        rs.rs_partition(rs.RS_KEY_F32, rs.RS_OP_GT, 0, A, B, C, None, D, 64, T, 1 << 20, stream=0)
+    assert ei.value.status == rs.RS_ERR_INVALID_VALUE
+    with pytest.raises(rs.RsError) as ei:   # output overlaps the values
+        rs.rs_partition(rs.RS_KEY_F32, rs.RS_OP_GT, 0, A, C + 64, C, D, D + (1 << 20), 64, T,
+                        1 << 20, stream=0)
+    assert ei.value.status == rs.RS_ERR_OVERLAP
+    q1 = rs.rs_select(rs.RS_KEY_I32, rs.RS_OP_EQ, 5, None, None, None, None, None, 1 << 20, None, 0)
+    q2 = rs.rs_partition(rs.RS_KEY_U32, rs.RS_OP_NE, 9, None, None, None, None, None, 1 << 20,
+                         None, 0)
+    assert q1 == q2 > 0
