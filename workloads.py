@@ -23,6 +23,18 @@ Recipes (seed 0 unless stated):
   of ``n // 256`` each, taken in order from one ``rng.permutation(n)``, are set
   to -0.0, +0.0, +1e-38 (bits 0x006CE3EE, subnormal) and -1e-38 (0x806CE3EE).
 * values for key-value sorts: ``arange(n, dtype=uint32)`` (original index).
+* ``splat_pairs(gaussians)``: screen-space splats for a tile renderer (the
+  pages introduce radix sort as the sorting step of a Gaussian-splatting
+  renderer; the key layout below is this build's synthetic stand-in, no
+  scene is used).  A 1920 x 1080 screen in 16 x 16-pixel tiles (120 x 68 =
+  8160 tiles, 13 bits of tile id).  Each splat has a centre drawn uniformly
+  over the screen (70 %) or from 8 Gaussian clusters of sigma 80 pixels
+  (30 %, clipped to the screen), a radius of 2 + 30 * u^3 pixels (u uniform,
+  so most splats are small) and a depth uniform in [0.2, 100).  It emits one
+  entry per tile its bounding square touches: key = tile id * 2^32 + the
+  bit pattern of the float depth (positive floats order as their patterns),
+  value = the splat's index.  Sorting the keys on bits [0, 32 + 13) groups
+  the entries by tile and orders each tile front to back.
 """
 import numpy as np
 
@@ -130,3 +142,40 @@ def float_pairs(n=N_FLOAT_PAIRS, seed=SEED):
 
 def headline_pairs(n=N_HEADLINE, seed=SEED):
     return uniform_u32(n, seed), index_values(n)
+
+
+# --- tile/depth keys of a splat renderer ------------------------------------------------
+
+SPLAT_W, SPLAT_H, SPLAT_TILE = 1920, 1080, 16
+SPLAT_TILES_X = (SPLAT_W + SPLAT_TILE - 1) // SPLAT_TILE
+SPLAT_TILES_Y = (SPLAT_H + SPLAT_TILE - 1) // SPLAT_TILE
+SPLAT_TILE_BITS = int(np.ceil(np.log2(SPLAT_TILES_X * SPLAT_TILES_Y)))
+
+
+def splat_pairs(gaussians, seed=SEED):
+    """(keys uint64, values uint32) for `gaussians` splats (see the module notes)."""
+    rng = rng_for(seed)
+    cx = rng.random(gaussians) * SPLAT_W
+    cy = rng.random(gaussians) * SPLAT_H
+    clustered = rng.random(gaussians) < 0.3
+    centres = rng.random((8, 2)) * np.array([SPLAT_W, SPLAT_H])
+    which = rng.integers(0, 8, gaussians)
+    jitter = rng.standard_normal((gaussians, 2)) * 80.0
+    cx = np.where(clustered, np.clip(centres[which, 0] + jitter[:, 0], 0, SPLAT_W - 1), cx)
+    cy = np.where(clustered, np.clip(centres[which, 1] + jitter[:, 1], 0, SPLAT_H - 1), cy)
+    radius = 2.0 + 30.0 * rng.random(gaussians) ** 3
+    depth = (0.2 + rng.random(gaussians) * 99.8).astype(np.float32)
+    tx0 = np.clip(((cx - radius) // SPLAT_TILE).astype(np.int64), 0, SPLAT_TILES_X - 1)
+    tx1 = np.clip(((cx + radius) // SPLAT_TILE).astype(np.int64), 0, SPLAT_TILES_X - 1)
+    ty0 = np.clip(((cy - radius) // SPLAT_TILE).astype(np.int64), 0, SPLAT_TILES_Y - 1)
+    ty1 = np.clip(((cy + radius) // SPLAT_TILE).astype(np.int64), 0, SPLAT_TILES_Y - 1)
+    wx = tx1 - tx0 + 1
+    wy = ty1 - ty0 + 1
+    count = wx * wy
+    owner = np.repeat(np.arange(gaussians, dtype=np.int64), count)
+    local = np.arange(owner.size, dtype=np.int64) - np.repeat(np.cumsum(count) - count, count)
+    tx = tx0[owner] + local % wx[owner]
+    ty = ty0[owner] + local // wx[owner]
+    tile = (ty * SPLAT_TILES_X + tx).astype(np.uint64)
+    keys = (tile << np.uint64(32)) | depth.view(np.uint32)[owner].astype(np.uint64)
+    return keys, owner.astype(np.uint32)
