@@ -423,6 +423,31 @@ def record_traffic(name, fetch_dir, write_dir):
     print(json.dumps({name: entry}))
 
 
+def copy_ceiling(steps=20):
+    """Device-to-device copy of 1 GiB (torch's copy kernel) timed with HIP
+    events: the bandwidth a kernel that reads and writes every byte once
+    reaches on this GPU, as context for the passes' roofline fractions."""
+    import torch
+    dev = torch.device("cuda:0")
+    a = torch.empty(1 << 28, dtype=torch.int32, device=dev).fill_(1)
+    b = torch.empty_like(a)
+    for _ in range(3):
+        b.copy_(a)
+    torch.cuda.synchronize()
+    start = torch.cuda.Event(enable_timing=True)
+    stop = torch.cuda.Event(enable_timing=True)
+    start.record()
+    for _ in range(steps):
+        b.copy_(a)
+    stop.record()
+    torch.cuda.synchronize()
+    ms = start.elapsed_time(stop) / steps
+    moved = 2 * a.numel() * 4
+    return {"metric": "device copy of 1 GiB (read + write)", "ms_per_copy": round(ms, 5),
+            "GB/s": round(moved / (ms * 1e-3) / 1e9, 1),
+            "frac_of_8TBps": round(moved / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4), "steps": steps}
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -434,6 +459,8 @@ def main():
     ap.add_argument("--no-check", action="store_true")
     ap.add_argument("--copy-calibration", action="store_true",
                     help="also run a plain 1 GiB device copy (reference for HBM counters)")
+    ap.add_argument("--copy-ceiling", action="store_true",
+                    help="time a 1 GiB device copy and print its bandwidth (context only)")
     ap.add_argument("--record-traffic", nargs=2, metavar=("FETCH_DIR", "WRITE_DIR"),
                     help="write profiles/traffic.json for --workload from two rocprofv3 --pmc "
                          "output folders (FETCH_SIZE, WRITE_SIZE) and exit; no GPU needed")
@@ -441,6 +468,9 @@ def main():
 
     if args.record_traffic:
         record_traffic(args.workload, *args.record_traffic)
+        return
+    if args.copy_ceiling:
+        print(json.dumps(copy_ceiling()), flush=True)
         return
     if args.gpus != 1:
         print("bench.py measures one GPU only: this library has no multi-GPU path "
