@@ -59,6 +59,13 @@ WORKLOADS = {
     "tile_bitonic_1024": ("1024 uniform u32 keys, one LDS bitonic tile", "bitonic", 1024, 0, 32),
     "tile_radix_1024": ("1024 uniform u32 keys, keys-only radix sort (4 passes)",
                         "keys_u32", 1024, 0, 32),
+    "pairs_u64_2p27": ("uniform u64 keys with index values, n=2^27, bits [0,64), 8 passes",
+                       "pairs_u64", 1 << 27, 0, 64),
+    "splat_pairs_2p22": ("splat tile/depth u64 keys of 2^22 splats (1920x1080, 16x16 tiles), "
+                         "splat-index values, bits [0,45), 6 passes", "pairs_u64", 1 << 22, 0, 45),
+    "scan_u32_2p28": ("exclusive prefix sum of 2^28 uniform u32 (mod 2^32)", "scan", 1 << 28, 0, 0),
+    "partition_f32_2p28": ("stable partition x > 0 of the 2^28 compaction input with index values",
+                           "partition", 1 << 28, 0, 0),
 }
 DEFAULT = "pairs_u32_2p28"
 
@@ -81,6 +88,15 @@ def make_inputs(name):
         return workloads.pairs_zipf(n)
     if kind == "compact":
         return workloads.compact_input(n), None
+    if kind == "partition":
+        return workloads.compact_input(n), workloads.index_values(n)
+    if kind == "scan":
+        return workloads.uniform_u32(n), None
+    if name == "splat_pairs_2p22":
+        return workloads.splat_pairs(n)
+    if kind == "pairs_u64":
+        rng = workloads.rng_for()
+        return rng.integers(0, 2**64, n, dtype="uint64"), workloads.index_values(n)
     if n == 1024:
         return workloads.tile_keys(), None
     keys, vals = workloads.headline_pairs(n)
@@ -121,6 +137,12 @@ def cpu_baseline(name, keys, vals, budget_s=10.0, sample=None):
         t0 = time.perf_counter()
         if kind == "compact":
             oracle.compact_positive_f32(k)
+        elif kind == "scan":
+            oracle.scan_u32(k)
+        elif kind == "partition":
+            oracle.select(k, ">", 0.0, v, partition=True)
+        elif kind == "pairs_u64":
+            oracle.sort_u64(k, v, b, e)
         elif kind == "bitonic":
             oracle.bitonic_tile(k, 1024, b, e)
         elif kind == "pairs_f32":
@@ -132,12 +154,66 @@ def cpu_baseline(name, keys, vals, budget_s=10.0, sample=None):
         if total >= budget_s or runs >= (1000 if k.size <= 4096 else 50):
             break
     per_run = total / runs
-    unit = "G elements/s" if kind == "compact" else "Gkeys/s"
+    unit = "G elements/s" if kind in ("compact", "scan", "partition") else "Gkeys/s"
     host_cores, model = host_cpu()
     return {"value": round(k.size / per_run / 1e9, 6), "unit": unit, "cores": 1, "kind": "oracle",
             "sample": "%s, %d run(s), %.4f s each; single-threaded C oracle (gcc -O2)"
                       % (what, runs, per_run),
             "host_cores": host_cores, "host_cpu": model}
+
+
+def f32_order(bits):
+    """Unsigned order patterns of float32 bit patterns (IEEE totalOrder)."""
+    import numpy as np
+    neg = (bits >> np.uint32(31)) != 0
+    return np.where(neg, ~bits, bits | np.uint32(0x80000000))
+
+
+def check_output(kind, keys, vals, k_h, v_h, count, b, e):
+    """Properties that define each output uniquely, with numpy only."""
+    import numpy as np
+    if kind in ("compact", "partition"):
+        x = keys.view(np.float32)
+        keep = x > np.float32(0)
+        k = int(keep.sum())
+        got = k_h.view(np.uint32)
+        if count != k or not np.array_equal(got[:k], keys.view(np.uint32)[keep]):
+            return False
+        if kind == "compact":
+            return bool(np.all(got[k:] == 0))
+        return (np.array_equal(got[k:], keys.view(np.uint32)[~keep]) and
+                np.array_equal(v_h, np.concatenate([vals[keep], vals[~keep]])))
+    if kind == "scan":
+        ref = (np.cumsum(keys.astype(np.uint64)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+        return k_h[0] == 0 and np.array_equal(k_h[1:], ref[:-1])
+    if kind == "bitonic":
+        for s0 in range(0, keys.size, 1024):
+            if not np.array_equal(k_h[s0:s0 + 1024], np.sort(keys[s0:s0 + 1024], kind="stable")):
+                return False
+        return True
+    # sorts: non-decreasing field, key/value association, stability
+    raw = k_h.view(np.uint64 if kind == "pairs_u64" else np.uint32)
+    if kind == "pairs_f32":
+        order = f32_order(raw)
+    elif kind == "pairs_u64":
+        order = (raw >> np.uint64(b)) & np.uint64((1 << (e - b)) - 1)
+    elif e - b < 32:
+        order = raw & np.uint32(((1 << (e - b)) - 1) << b)
+    else:
+        order = raw
+    ok = bool(np.all(order[1:] >= order[:-1]))
+    if v_h is None:
+        return ok
+    src = keys.view(raw.dtype)
+    if np.array_equal(vals, np.arange(vals.size, dtype=np.uint32)):
+        # values are positions: association and stability
+        ok = ok and bool(np.array_equal(raw, src[v_h]))
+        eq = order[1:] == order[:-1]
+        return ok and bool(np.all(v_h[1:][eq] > v_h[:-1][eq]))
+    # other values: the stable order by numpy's stable argsort of the field
+    field = (src >> np.uint64(b)) & np.uint64((1 << (e - b)) - 1) if kind == "pairs_u64" else None
+    perm = np.argsort(field, kind="stable")
+    return ok and bool(np.array_equal(raw, src[perm])) and bool(np.array_equal(v_h, vals[perm]))
 
 
 def timed_region(step, steps, warmup, stream):
@@ -217,20 +293,28 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
     keys, vals = make_inputs(name)
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
-    is_f32 = kind in ("pairs_f32", "compact")
+    is_f32 = kind in ("pairs_f32", "compact", "partition")
     kin = torch.from_numpy(keys.view(np.float32) if is_f32 else keys).to(dev)
     vin = torch.from_numpy(vals).to(dev) if vals is not None else None
     kout = torch.empty_like(kin)
     vout = torch.empty_like(vin) if vin is not None else None
     count = torch.empty(1, dtype=torch.uint32, device=dev)
+    gt0 = 0   # bit pattern of the threshold 0.0f
     if kind == "pairs_u32":
         need = rs.rs_sort_pairs_u32(None, None, None, None, n, b, e, None, 0)
     elif kind == "pairs_f32":
         need = rs.rs_sort_pairs_f32(None, None, None, None, n, b, e, None, 0)
     elif kind == "keys_u32":
         need = rs.rs_sort_keys_u32(None, None, n, b, e, None, 0)
+    elif kind == "pairs_u64":
+        need = rs.rs_sort_pairs(rs.RS_KEY_U64, 0, None, None, None, None, n, b, e, None, 0)
     elif kind == "compact":
         need = rs.rs_compact_positive_f32(None, None, None, n, None, 0)
+    elif kind == "scan":
+        need = rs.rs_exclusive_scan_u32(None, None, n, None, 0)
+    elif kind == "partition":
+        need = rs.rs_partition(rs.RS_KEY_F32, rs.RS_OP_GT, gt0, None, None, vin, vout, None, n,
+                               None, 0)
     else:
         need = 0
     temp = torch.empty(max(need, 1), dtype=torch.uint8, device=dev)
@@ -242,8 +326,15 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
             rs.rs_sort_pairs_f32(kin, kout, vin, vout, n, b, e, temp, need, stream)
         elif kind == "keys_u32":
             rs.rs_sort_keys_u32(kin, kout, n, b, e, temp, need, stream)
+        elif kind == "pairs_u64":
+            rs.rs_sort_pairs(rs.RS_KEY_U64, 0, kin, kout, vin, vout, n, b, e, temp, need, stream)
         elif kind == "compact":
             rs.rs_compact_positive_f32(kin, kout, count, n, temp, need, stream)
+        elif kind == "scan":
+            rs.rs_exclusive_scan_u32(kin, kout, n, temp, need, stream)
+        elif kind == "partition":
+            rs.rs_partition(rs.RS_KEY_F32, rs.RS_OP_GT, gt0, kin, kout, vin, vout, count, n, temp,
+                            need, stream)
         else:
             rs.rs_bitonic_tile(kin, kout, n, 1024, b, e, stream)
 
@@ -260,43 +351,27 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
           flush=True)
 
     if check:
-        ok = True
-        k_h = kout.cpu().numpy()
-        if kind == "compact":
-            import oracle
-            ref, ref_count = oracle.compact_positive_f32(keys)
-            ok = (int(count.cpu().numpy()[0]) == ref_count and
-                  bool(np.array_equal(k_h.view(np.uint32), ref.view(np.uint32))))
-        elif kind == "bitonic":
-            import oracle
-            ok = bool(np.array_equal(k_h, oracle.bitonic_tile(keys, 1024, b, e)))
-        else:
-            if kind == "pairs_f32":
-                import oracle
-                order = oracle.f32_to_order(k_h.view(np.uint32))
-            elif e - b < 32:
-                order = k_h & np.uint32(((1 << (e - b)) - 1) << b)
-            else:
-                order = k_h
-            ok = bool(np.all(order[1:] >= order[:-1]))
-            if vout is not None:
-                v_h = vout.cpu().numpy()
-                kb = keys.view(np.uint32)
-                ok = ok and bool(np.array_equal(k_h.view(np.uint32), kb[v_h]))
-                eq = order[1:] == order[:-1]
-                ok = ok and bool(np.all(v_h[1:][eq] > v_h[:-1][eq]))
+        ok = check_output(kind, keys, vals, kout.cpu().numpy(),
+                          vout.cpu().numpy() if vout is not None else None,
+                          int(count.cpu().numpy()[0]), b, e)
         if not ok:
             print("bench: OUTPUT CHECK FAILED for %s" % name, file=sys.stderr, flush=True)
             sys.exit(1)
         print("bench: output check ok", file=sys.stderr, flush=True)
 
     passes = (e - b + 7) // 8
-    if kind == "compact":
-        dom, bytes_per = "compact", 8
+    if kind in ("compact", "bitonic", "scan"):
+        # read every element once, write every output element once
+        dom, bytes_per = {"compact": "compact", "bitonic": "bitonic", "scan": "scan"}[kind], 8
         algo_total = 8 * n
-    elif kind == "bitonic":
-        dom, bytes_per = "bitonic", 8
-        algo_total = 8 * n
+    elif kind == "partition":
+        # read and write every element and its value once (the counting read is an overhead)
+        dom, bytes_per = "select", 16
+        algo_total = 16 * n
+    elif kind == "pairs_u64":
+        # 8-byte key + 4-byte value, read and written by every pass
+        dom, bytes_per = "onesweep", 24
+        algo_total = 24 * n * passes
     elif n <= TILE_SORT_MAX:
         # the whole sort in one workgroup: the keys (and values) cross HBM once each way
         dom = "tile_sort"
@@ -327,6 +402,15 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
     if kind == "compact":
         metric, unit, value = ("G elements/s compacted (f32, n=2^28) and % of HBM roofline",
                                "G elements/s", n / (ms_per_step * 1e-3) / 1e9)
+    elif kind == "scan":
+        metric, unit, value = ("G elements/s prefix-summed (u32, n=2^28) and % of HBM roofline",
+                               "G elements/s", n / (ms_per_step * 1e-3) / 1e9)
+    elif kind == "partition":
+        metric, unit, value = ("G elements/s partitioned (f32 with u32 values, n=2^28) and % of "
+                               "HBM roofline", "G elements/s", n / (ms_per_step * 1e-3) / 1e9)
+    elif kind == "pairs_u64":
+        metric, unit, value = ("Gkeys/s sorted (u64 keys with u32 values) and % of HBM roofline",
+                               "Gkeys/s", n / (ms_per_step * 1e-3) / 1e9)
     elif kind == "bitonic" or n <= 4096:
         metric, unit, value = ("microseconds per call (1024-key tile)", "us", ms_per_step * 1e3)
     else:
@@ -345,10 +429,13 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         "vs_baseline": None,
         "dtype": {"pairs_u32": "u32", "keys_u32": "u32", "bitonic": "u32",
                   "pairs_f32": "f32 keys (bit-pattern integer ops), u32 values",
-                  "compact": "f32 (predicate on bit patterns)"}[kind],
+                  "compact": "f32 (predicate on bit patterns)", "scan": "u32",
+                  "partition": "f32 (IEEE comparison), u32 values",
+                  "pairs_u64": "u64 keys, u32 values"}[kind],
         "data": "synthetic",
         "config": {"workload": desc, "n": n, "begin_bit": b, "end_bit": e,
-                   "passes": passes if kind not in ("compact", "bitonic") else None},
+                   "passes": passes if kind not in ("compact", "bitonic", "scan", "partition")
+                   else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
                      "kernel": dom, "algorithmic_bytes_per_launch": algo_bytes,

@@ -65,3 +65,36 @@ def test_source_hash_is_stable_and_short():
     h = bench.source_hash()
     assert h == bench.source_hash()
     assert len(h) == 16 and all(c in "0123456789abcdef" for c in h)
+
+
+def test_output_checks_accept_correct_and_reject_broken_outputs():
+    import numpy as np
+    rng = np.random.default_rng(0)
+    n = 5000
+    keys = rng.integers(0, 2**32, n, dtype=np.uint32)
+    vals = np.arange(n, dtype=np.uint32)
+    perm = np.argsort(keys, kind="stable").astype(np.uint32)
+    assert bench.check_output("pairs_u32", keys, vals, keys[perm], perm, 0, 0, 32)
+    broken = perm.copy()
+    broken[[10, 11]] = broken[[11, 10]]
+    assert not bench.check_output("pairs_u32", keys, vals, keys[broken], broken, 0, 0, 32)
+    x = rng.standard_normal(n).astype(np.float32)
+    keep = x > 0
+    part = np.concatenate([x[keep], x[~keep]])
+    pv = np.concatenate([vals[keep], vals[~keep]])
+    assert bench.check_output("partition", x.view(np.uint32), vals, part, pv, int(keep.sum()), 0, 0)
+    assert not bench.check_output("partition", x.view(np.uint32), vals, part, pv[::-1].copy(),
+                                  int(keep.sum()), 0, 0)
+    comp = np.concatenate([x[keep], np.zeros((~keep).sum(), np.float32)])
+    assert bench.check_output("compact", x.view(np.uint32), None, comp, None, int(keep.sum()), 0, 0)
+    sc = (np.cumsum(keys.astype(np.uint64)) & np.uint64(0xFFFFFFFF)).astype(np.uint32)
+    exc = np.concatenate([[0], sc[:-1]]).astype(np.uint32)
+    assert bench.check_output("scan", keys, None, exc, None, 0, 0, 0)
+    assert not bench.check_output("scan", keys, None, sc, None, 0, 0, 0)
+    k64 = rng.integers(0, 2**45, n, dtype=np.uint64)
+    v64 = rng.integers(0, 100, n, dtype=np.uint32)     # values are not positions
+    p64 = np.argsort(k64, kind="stable")
+    assert bench.check_output("pairs_u64", k64, v64, k64[p64], v64[p64], 0, 0, 45)
+    f = rng.standard_normal(n).astype(np.float32)
+    fo = np.argsort(bench.f32_order(f.view(np.uint32)), kind="stable").astype(np.uint32)
+    assert bench.check_output("pairs_f32", f.view(np.uint32), vals, f[fo], fo, 0, 0, 32)
