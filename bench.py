@@ -61,8 +61,9 @@ WORKLOADS = {
                         "keys_u32", 1024, 0, 32),
     "pairs_u64_2p27": ("uniform u64 keys with index values, n=2^27, bits [0,64), 8 passes",
                        "pairs_u64", 1 << 27, 0, 64),
-    "splat_pairs_2p22": ("splat tile/depth u64 keys of 2^22 splats (1920x1080, 16x16 tiles), "
-                         "splat-index values, bits [0,45), 6 passes", "pairs_u64", 1 << 22, 0, 45),
+    "splat_pairs_2p22": ("splat tile/depth u64 keys of 2^22 splats (1920x1080, 16x16 tiles; "
+                         "24.2M tile entries), splat-index values, bits [0,45), 6 passes",
+                         "pairs_u64", 1 << 22, 0, 45),
     "scan_u32_2p28": ("exclusive prefix sum of 2^28 uniform u32 (mod 2^32)", "scan", 1 << 28, 0, 0),
     "partition_f32_2p28": ("stable partition x > 0 of the 2^28 compaction input with index values",
                            "partition", 1 << 28, 0, 0),
@@ -291,6 +292,7 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
     desc, kind, n, b, e = WORKLOADS[name]
     print("bench: generating %s" % name, file=sys.stderr, flush=True)
     keys, vals = make_inputs(name)
+    n = keys.size   # the splat workload's n counts splats; its arrays hold their tile entries
     dev = torch.device("cuda:0")
     stream = torch.cuda.current_stream()
     is_f32 = kind in ("pairs_f32", "compact", "partition")
