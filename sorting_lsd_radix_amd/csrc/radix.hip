@@ -326,6 +326,23 @@ struct PassArgs {
     // count of gate_bins[0..255] exceeds gate_cap, 2 only when one does.
     uint32_t gate, gate_cap;
     const uint32_t* gate_bins;
+    // Multi-pass launch (MULTI kernels: the hybrid sort's LSD fallback):
+    // every pass of the sort in one launch.  Tiles are handed out in (pass,
+    // tile) order from multi_counter[0]; multi_counter[1 + p] counts the
+    // finished tiles of pass p, and a tile of pass p > 0 starts only when
+    // every tile of pass p - 1 has finished.  Pass p reads m[p].src_*, writes
+    // m[p].dst_*, uses bins + 256 p and the zeroed states m_states + p *
+    // tiles * 256.
+    uint32_t multi_passes;
+    uint32_t* multi_counter;
+    uint32_t* m_states;
+    struct PassIo {
+        const uint32_t* src_keys;
+        uint32_t* dst_keys;
+        const uint32_t* src_vals;
+        uint32_t* dst_vals;
+        uint32_t shift, width;
+    } m[kMaxPasses];
 };
 
 // Loads the ITEMS keys of this lane for `tile`: row j of wave w is the 64
@@ -382,7 +399,8 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t k, uint32_t shift, uint32_
 // tiles the scheduler hands it.  Per tile: load, stable in-wave rank (LDS
 // atomics or ballots), tile counts and scans, decoupled look-back, re-layout
 // in digit order in LDS, scatter of each digit run.
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XF_IN, bool XF_OUT, bool KEY64>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XF_IN, bool XF_OUT, bool KEY64,
+          bool MULTI = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
 void onesweep_kernel(PassArgs a) {
     using Key = typename std::conditional<KEY64, uint64_t, uint32_t>::type;
@@ -405,14 +423,29 @@ void onesweep_kernel(PassArgs a) {
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t wave = tid / kWave;
+    // (the per-pass values below change between passes only in MULTI kernels)
     const uint32_t* __restrict__ src_keys = a.src_keys;
     uint32_t* __restrict__ dst_keys = a.dst_keys;
     const uint32_t* __restrict__ src_vals = a.src_vals;
     uint32_t* __restrict__ dst_vals = a.dst_vals;
     uint32_t* __restrict__ states = a.states;
-    const uint32_t n = a.n, shift = a.shift, width = a.width, tiles = a.tiles;
-    const uint32_t last_digit = (1u << width) - 1u;
+    const uint32_t n = a.n, tiles = a.tiles;
+    uint32_t shift = a.shift, width = a.width;
+    uint32_t last_digit = (1u << width) - 1u;
     const uint32_t group = blockIdx.x % a.groups;
+    uint32_t cur_pass = 0;
+    bool xf_in = XF_IN, xf_out = XF_OUT;   // uniform
+    if constexpr (MULTI) {
+        src_keys = a.m[0].src_keys;
+        dst_keys = a.m[0].dst_keys;
+        src_vals = a.m[0].src_vals;
+        dst_vals = a.m[0].dst_vals;
+        states = a.m_states;
+        shift = a.m[0].shift;
+        width = a.m[0].width;
+        last_digit = (1u << width) - 1u;
+        xf_out = XF_OUT && a.multi_passes == 1;
+    }
 
     if (a.gate != 0) {   // uniform: a gated launch of the hybrid sort
         const uint32_t c = (tid < kRadix) ? a.gate_bins[tid] : 0u;
@@ -421,16 +454,16 @@ void onesweep_kernel(PassArgs a) {
     }
 
     // global digit count of this pass (thread d holds digit d)
-    const uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
+    uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
     // Same-address LDS atomics serialise, so the atomic rank below is used
     // while no digit holds more than a share 2^-atomic_limit_log2 of the
     // pass's keys, and for a tile only if the block's previous tile had no
     // digit over that share of its keys (earlier passes gather equal keys
     // into runs, which then collide within a row); otherwise the ballot rank.
 #ifdef RS_FORCE_BALLOT_RANK
-    const bool spread = false;   // build switch: ballot rank on every tile
+    bool spread = false;   // build switch: ballot rank on every tile
 #else
-    const bool spread = !__syncthreads_or((static_cast<uint64_t>(bin) << a.atomic_limit_log2) > n);
+    bool spread = !__syncthreads_or((static_cast<uint64_t>(bin) << a.atomic_limit_log2) > n);
 #endif
     bool atomic_rank = spread;   // uniform
 
@@ -439,15 +472,50 @@ void onesweep_kernel(PassArgs a) {
         // time from taking a tile to publishing its count delays every later
         // tile's look-back.
         if (tid == 0) {
-            s_next = next_chunked_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
+            if constexpr (MULTI) s_next = fetch_add_agent(&a.multi_counter[0], 1u);
+            else s_next = next_chunked_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
             s_crowded = 0u;   // the previous tile's readers all passed a barrier since
         }
         // Only this wave reads and writes its counters during the rank, and the
         // previous tile's readers of s_off all passed a barrier since.
         for (uint32_t i = lane; i < kRadix; i += kWave) s_off[wave * kRadix + i] = 0u;
         __syncthreads();
-        const uint32_t tile = s_next;
-        if (tile >= tiles) break;   // uniform: no tiles left
+        uint32_t tile = s_next;
+        if constexpr (MULTI) {
+            if (tile >= tiles * a.multi_passes) break;   // uniform: no tiles left
+            const uint32_t p = tile / tiles;
+            tile -= p * tiles;
+            if (p != cur_pass) {   // uniform; a block's passes only increase
+                // Every tile of pass p - 1 has been handed out (smaller ids) to
+                // running blocks; wait until all of them have finished, then
+                // take their stores in (agent-scope acquire after their release).
+                if (tid == 0) {
+                    while (load_state(&a.multi_counter[p]) < tiles) __builtin_amdgcn_s_sleep(2);
+                    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "agent");
+                }
+                cur_pass = p;
+                src_keys = a.m[p].src_keys;
+                dst_keys = a.m[p].dst_keys;
+                src_vals = a.m[p].src_vals;
+                dst_vals = a.m[p].dst_vals;
+                states = a.m_states + static_cast<size_t>(p) * tiles * kRadix;
+                shift = a.m[p].shift;
+                width = a.m[p].width;
+                last_digit = (1u << width) - 1u;
+                xf_in = false;
+                xf_out = XF_OUT && p + 1 == a.multi_passes;
+                bin = (tid < kRadix) ? a.bins[p * kRadix + tid] : 0u;
+#ifdef RS_FORCE_BALLOT_RANK
+                spread = false;
+                __syncthreads();
+#else
+                spread = !__syncthreads_or((static_cast<uint64_t>(bin) << 4) > n);
+#endif
+                atomic_rank = spread;
+            }
+        } else {
+            if (tile >= tiles) break;   // uniform: no tiles left
+        }
         Key k[ITEMS];
         if constexpr (KEY64) {
             if (a.soa_in) {
@@ -466,7 +534,7 @@ void onesweep_kernel(PassArgs a) {
         const uint32_t valid = (n - tile_base < static_cast<uint32_t>(TILE)) ? n - tile_base : TILE;
         const bool full = (valid == static_cast<uint32_t>(TILE));
         const uint32_t first = tile_base + wave * WAVE_KEYS + lane;
-        if (XF_IN) {
+        if (XF_IN && xf_in) {
 #pragma unroll
             for (int j = 0; j < ITEMS; ++j) {
                 if constexpr (KEY64) k[j] = xform64(k[j], a.xin);
@@ -659,7 +727,7 @@ void onesweep_kernel(PassArgs a) {
             }
             const uint32_t dst = min(i + s_adjust[d], n);
             if constexpr (KEY64) {
-                if (XF_OUT) key = xform64(key, a.xout);
+                if (XF_OUT && xf_out) key = xform64(key, a.xout);
                 const uint32_t lo = static_cast<uint32_t>(key), hi = static_cast<uint32_t>(key >> 32);
                 if (soa_out) {
                     __builtin_amdgcn_raw_buffer_store_b32(lo, out_keys, static_cast<int>(dst * 4u), 0, 0);
@@ -669,8 +737,8 @@ void onesweep_kernel(PassArgs a) {
                                                           static_cast<int>(dst * 8u), 0, 0);
                 }
             } else {
-                __builtin_amdgcn_raw_buffer_store_b32(XF_OUT ? xform32(key, a.xout) : key, out_keys,
-                                                      static_cast<int>(dst * 4u), 0, 0);
+                __builtin_amdgcn_raw_buffer_store_b32((XF_OUT && xf_out) ? xform32(key, a.xout) : key,
+                                                      out_keys, static_cast<int>(dst * 4u), 0, 0);
             }
             if (PAIRS && r % 4 == 3) __builtin_amdgcn_sched_barrier(0);   // bounds live registers
         }
@@ -687,6 +755,17 @@ void onesweep_kernel(PassArgs a) {
                 const uint32_t d = (digits[r / 4] >> (8 * (r % 4))) & 0xFFu;
                 const uint32_t dst = min(i + s_adjust[d], n);
                 __builtin_amdgcn_raw_buffer_store_b32(s_vbuf[i], out_vals, static_cast<int>(dst * 4u), 0, 0);
+            }
+        }
+        if constexpr (MULTI) {
+            // this tile of pass cur_pass is done: every wave's stores have
+            // completed, then one agent-scope release makes them visible to
+            // the blocks that wait on the pass's count
+            __builtin_amdgcn_s_waitcnt(0);
+            __syncthreads();
+            if (tid == 0) {
+                __builtin_amdgcn_fence(__ATOMIC_RELEASE, "agent");
+                fetch_add_agent(&a.multi_counter[1 + cur_pass], 1u);
             }
         }
         // the next iteration rewrites s_buf and s_adjust only after a barrier
@@ -976,8 +1055,10 @@ __global__ __launch_bounds__(kBucketBlock) void bucket_sort_kernel(BucketArgs a)
 //   tmp_keys2 [n] keys   second key buffer of a two-key sort (its outputs are
 //                        two word arrays, so its passes ping-pong in temp)
 // bins, sched and states0 are contiguous and cleared by one fill launch.
+//   multi    [64]           u32   multi-pass counters, and states_m [4][tiles][256]:
+//                                  the hybrid sort's fallback (sizes it can take)
 struct SortLayout {
-    size_t bins, sched, states0, states1, tmp_keys, tmp_vals, tmp_keys2, total;
+    size_t bins, sched, multi, states0, states_m, states1, tmp_keys, tmp_vals, tmp_keys2, total;
     uint64_t clear_words;
     uint32_t tiles;
 };
@@ -1009,6 +1090,11 @@ uint64_t pass_tile_keys(uint64_t n, bool pairs, bool key64) {
     }
 }
 
+// Sizes the hybrid sort takes (4-byte keys; it also needs two or more passes).
+bool hybrid_size(uint64_t n, const SortKind& kind) {
+    return !kind.key64 && n > kTileSortMax && n <= kHybridMaxN;
+}
+
 SortLayout sort_layout(uint64_t n, bool pairs, const SortKind& kind) {
     SortLayout L{};
     const int max_passes = kind.key64 ? kMaxPasses64 : kMaxPasses;
@@ -1021,8 +1107,12 @@ SortLayout sort_layout(uint64_t n, bool pairs, const SortKind& kind) {
     off += align_up(static_cast<size_t>(max_passes) * kRadix * 4);
     L.sched = off;
     off += static_cast<size_t>(max_passes) * kSchedWords * 4;
+    L.multi = off;
+    off += kSchedWords * 4;
     L.states0 = off;
     off += states_bytes;
+    L.states_m = off;
+    if (hybrid_size(n, kind)) off += static_cast<size_t>(kMaxPasses) * states_bytes;
     L.clear_words = off / 4;
     L.states1 = off;
     off += states_bytes;   // every sort path has at least two passes' worth of states
@@ -1065,6 +1155,24 @@ hipError_t launch_pass_items(bool xf_in, bool xf_out, const PassArgs& a, hipStre
     if (xf_in) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, false, KEY64>(a, s);
     if (xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, true, KEY64>(a, s);
     return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false, KEY64>(a, s);
+}
+
+// The hybrid sort's fallback: every LSD pass in one launch of the small shape.
+template <bool PAIRS, bool XF>
+hipError_t launch_multi_t(const PassArgs& a, hipStream_t s) {
+    auto kern = onesweep_kernel<kSortBlock, kSortItems, kSortLookback, PAIRS, XF, XF, false, true>;
+    static const uint32_t resident = resident_blocks(kern, kSortBlock);   // one-time init
+    const uint32_t grid = a.tiles < resident ? a.tiles : resident;
+    PassArgs b = a;
+    b.groups = 1;
+    b.chunk_log2 = 0;
+    kern<<<dim3(grid), kSortBlock, 0, s>>>(b);
+    return hipGetLastError();
+}
+
+hipError_t launch_multi(bool pairs, bool xf, const PassArgs& a, hipStream_t s) {
+    if (pairs) return xf ? launch_multi_t<true, true>(a, s) : launch_multi_t<true, false>(a, s);
+    return xf ? launch_multi_t<false, true>(a, s) : launch_multi_t<false, false>(a, s);
 }
 
 template <bool PAIRS>
@@ -1258,10 +1366,11 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
 
     // Hybrid sort of a small input: the top digit's pass into temp, then one
     // workgroup per bucket; both run only if no bucket of the top digit
-    // holds more than kBucketCap keys, and the LSD passes below only if one
-    // does (every launch reads the same counts, so exactly one path runs).
+    // holds more than kBucketCap keys, and the LSD passes (all in one
+    // multi-pass launch) only if one does (every launch reads the same
+    // counts, so exactly one path runs).
     const int top = passes - 1;
-    const bool hybrid = !kind.key64 && passes >= 2 && n <= kHybridMaxN;
+    const bool hybrid = hybrid_size(n, kind) && passes >= 2;
     if (hybrid) {
         PassArgs a{};
         a.src_keys = io.keys_in;
@@ -1311,6 +1420,39 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
         if (e != hipSuccess) return e;
     }
 
+    if (hybrid) {
+        PassArgs a{};
+        a.n = n;
+        a.tiles = L.tiles;
+        a.bins = bins;
+        a.atomic_limit_log2 = 1u;   // pass 0 reads the input order
+        a.xin = kind.xf;
+        a.xout = xout;
+        a.gate = 2u;
+        a.gate_cap = kBucketCap;
+        a.gate_bins = bins + top * kRadix;
+        a.multi_passes = static_cast<uint32_t>(passes);
+        a.multi_counter = reinterpret_cast<uint32_t*>(base + L.multi);
+        a.m_states = reinterpret_cast<uint32_t*>(base + L.states_m);
+        const uint32_t* sk = io.keys_in;
+        const uint32_t* sv = io.vals_in;
+        for (int p = 0; p < passes; ++p) {
+            const bool to_out = ((passes - 1 - p) % 2) == 0;
+            a.m[p].src_keys = sk;
+            a.m[p].src_vals = sv;
+            a.m[p].dst_keys = to_out ? io.keys_out : tmp_keys;
+            a.m[p].dst_vals = pairs ? (to_out ? io.vals_out : tmp_vals) : nullptr;
+            a.m[p].shift = pd.shift[p];
+            a.m[p].width = pd.width[p];
+            sk = a.m[p].dst_keys;
+            sv = a.m[p].dst_vals;
+        }
+        timing_before(stream, RS_KERNEL_ONESWEEP);
+        e = launch_multi(pairs, kind.transforms, a, stream);
+        timing_after(stream);
+        return e;
+    }
+
     const uint32_t* sk = io.keys_in;
     const uint32_t* sv = io.vals_in;
     for (int p = 0; p < passes; ++p) {
@@ -1345,11 +1487,6 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
         a.atomic_limit_log2 = (p == 0) ? 1u : 4u;
         a.xin = kind.xf;
         a.xout = xout;
-        if (hybrid) {   // the fallback of the hybrid sort
-            a.gate = 2u;
-            a.gate_cap = kBucketCap;
-            a.gate_bins = bins + top * kRadix;
-        }
         const bool xf_in = kind.transforms && p == 0;
         const bool xf_out = kind.transforms && last;
         timing_before(stream, RS_KERNEL_ONESWEEP);

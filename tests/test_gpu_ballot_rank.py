@@ -56,9 +56,9 @@ def test_ballot_keys_u32(n):
         assert np.array_equal(gpu_sort_keys_u32(keys, b, e), oracle.sort_u32(keys, None, b, e))
 
 
+@pytest.mark.parametrize("n", [100000, PLARGE + 1234])
 @pytest.mark.parametrize("kind", ["card24", "zipf", "all_equal", "few_values"])
-def test_ballot_distributions(kind):
-    n = PLARGE + 1234
+def test_ballot_distributions(kind, n):
     print("ballot build: pairs distribution=%s n=%d" % (kind, n), flush=True)
     keys = dist_keys(kind, n)
     vals = np.arange(n, dtype=np.uint32)
