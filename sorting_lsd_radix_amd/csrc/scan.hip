@@ -8,7 +8,7 @@
 // "WebGPU Unleashed", 4.1: a digit pass as a prefix sum of occurrences).
 //
 //  * rs_exclusive_scan_u32 / rs_inclusive_scan_u32: one pass; each tile of
-//    16384 elements publishes its sum, then looks back over earlier tiles'
+//    32768 elements publishes its sum, then looks back over earlier tiles'
 //    published sums until it meets an inclusive prefix (64-bit state words:
 //    two status bits above a 32-bit sum, so sums wrap modulo 2^32 like the
 //    elements');
@@ -29,8 +29,8 @@ namespace rs {
 namespace {
 
 constexpr int kScanBlock = 1024;
-constexpr int kScanQuads = 4;                                   // 16-byte vectors per thread
-constexpr int kScanTile = kScanBlock * kScanQuads * 4;          // 16384 elements
+constexpr int kScanQuads = 8;                                   // 16-byte vectors per thread
+constexpr int kScanTile = kScanBlock * kScanQuads * 4;          // 32768 elements
 constexpr uint64_t kScanAggregate = 1ull << 32;                 // the tile's own sum is ready
 constexpr uint64_t kScanPrefix = 2ull << 32;                    // the inclusive prefix is ready
 
@@ -72,8 +72,11 @@ __device__ uint32_t scan_look_back(uint64_t* states, uint32_t tile, uint32_t lan
 
 // ---------------------------------------------------------------------------
 // Prefix sum.  Thread t of a tile holds the 16-byte vectors q * 1024 + t,
-// q = 0..3, i.e. vector row q of the tile is the 4096 elements q*4096 ..;
-// element order within the tile is (row, thread, element).
+// q = 0..7, i.e. vector row q of the tile is the 4096 elements q*4096 ..;
+// element order within the tile is (row, thread, element).  Each wave scans
+// its share of every row; wave 0 then scans the 128 (row, wave) totals in
+// that order, publishes the tile's sum, looks back and hands every wave its
+// offsets.
 // ---------------------------------------------------------------------------
 template <bool INCLUSIVE>
 __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __restrict__ in,
@@ -82,7 +85,9 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
                                                           uint32_t* __restrict__ sched, uint32_t groups,
                                                           uint32_t chunk_log2) {
     constexpr int WAVES = kScanBlock / kWave;
-    __shared__ uint32_t s_wave[kScanQuads][WAVES];   // per row: each wave's total
+    constexpr int PARTS = kScanQuads * WAVES;          // (row, wave) totals, row-major
+    static_assert(PARTS % kWave == 0, "wave 0 scans the totals in lane-sized groups");
+    __shared__ uint32_t s_part[PARTS];                 // totals, then exclusive offsets in the tile
     __shared__ uint32_t s_tile;
     __shared__ uint32_t s_excl;
 
@@ -120,7 +125,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
             }
         }
 
-        // inclusive sums inside each vector, the vector's total scanned over the wave
+        // inclusive sums inside each vector, the vectors' totals scanned over the wave
         uint32_t wave_excl[kScanQuads];
 #pragma unroll
         for (int q = 0; q < kScanQuads; ++q) {
@@ -129,31 +134,24 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
             x[q][3] += x[q][2];
             const uint32_t inc = wave_inclusive_sum(x[q][3]);
             wave_excl[q] = inc - x[q][3];
-            if (lane == kWave - 1) s_wave[q][wave] = inc;
+            if (lane == kWave - 1) s_part[q * WAVES + wave] = inc;
         }
         __syncthreads();
 
-        // this thread's offset inside the tile: earlier rows, then earlier waves of its row
-        uint32_t row_before = 0, tile_total = 0;
-        uint32_t wave_before[kScanQuads];
-#pragma unroll
-        for (int q = 0; q < kScanQuads; ++q) {
-            uint32_t row = 0, before = 0;
-#pragma unroll
-            for (int w = 0; w < WAVES; ++w) {
-                const uint32_t c = s_wave[q][w];
-                if (w < static_cast<int>(wave)) before += c;
-                row += c;
-            }
-            wave_before[q] = row_before + before;
-            row_before += row;
-        }
-        tile_total = row_before;
-        if (tid == 0)
-            store_state64(&states[tile], (tile == 0 ? kScanPrefix : kScanAggregate) | tile_total);
-
         if (wave == 0) {
+            // exclusive offsets of the (row, wave) parts inside the tile
+            uint32_t carry = 0;
+#pragma unroll
+            for (int g = 0; g < PARTS / kWave; ++g) {
+                const uint32_t v = s_part[g * kWave + lane];
+                const uint32_t inc = wave_inclusive_sum(v);
+                s_part[g * kWave + lane] = carry + inc - v;
+                carry += __shfl(inc, kWave - 1, kWave);
+            }
+            const uint32_t tile_total = carry;
             uint32_t excl = 0;
+            if (lane == 0)
+                store_state64(&states[tile], (tile == 0 ? kScanPrefix : kScanAggregate) | tile_total);
             if (tile > 0) {
                 excl = scan_look_back(states, tile, lane);
                 if (lane == 0) store_state64(&states[tile], kScanPrefix | static_cast<uint32_t>(excl + tile_total));
@@ -165,7 +163,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
 
 #pragma unroll
         for (int q = 0; q < kScanQuads; ++q) {
-            const uint32_t off = excl + wave_before[q] + wave_excl[q];
+            const uint32_t off = excl + s_part[q * WAVES + wave] + wave_excl[q];
             u32x4 v;
             // x[q][e] holds the inclusive sum of the vector's elements 0..e
             if (INCLUSIVE) {
@@ -189,7 +187,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
                 __builtin_amdgcn_raw_buffer_store_b32(v.w, out_rsrc, static_cast<int>((e0 + 3) * 4u), 0, 0);
             }
         }
-        // s_wave and s_excl are rewritten only after the next loop-top barrier
+        // s_part and s_excl are rewritten only after the next loop-top barrier
     }
 }
 

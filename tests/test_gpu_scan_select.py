@@ -1,6 +1,6 @@
 """Prefix sums, select and stable partition on the GPU, bit for bit against the oracle.
 
-The scan is one pass with a decoupled look-back over 16384-element tiles
+The scan is one pass with a decoupled look-back over 32768-element tiles
 (64-bit tile states; sums wrap modulo 2^32).  Select and partition
 generalise the compaction: any of six comparisons on u32, i32 or f32
 elements, optional values, 32768- (16384- with values) element tiles; the
@@ -17,7 +17,7 @@ from gpu_helpers import _raw, gpu_scan, gpu_select
 
 pytestmark = pytest.mark.gpu
 
-ST = 16384    # scan tile
+ST = 32768    # scan tile
 SEL = 32768   # select tile without values (16384 with)
 
 
