@@ -110,4 +110,21 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return x;
 }
 
+// Inclusive sum over the 64 lanes of a wave with DPP moves instead of LDS
+// crossbar shuffles: a Hillis-Steele scan inside each row of 16 lanes
+// (shifts by 1, 2, 4, 8, zeros shifted in), then row 15's total broadcast into
+// rows 1 and 3 and lane 31's into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_sum_dpp(uint32_t x) {
+    constexpr int kRowShr = 0x110;      // row_shr:n is kRowShr + n
+    constexpr int kRowBcast15 = 0x142;
+    constexpr int kRowBcast31 = 0x143;
+    x += __builtin_amdgcn_update_dpp(0u, x, kRowShr + 1, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, kRowShr + 2, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, kRowShr + 4, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, kRowShr + 8, 0xF, 0xF, true);
+    x += __builtin_amdgcn_update_dpp(0u, x, kRowBcast15, 0xA, 0xF, false);
+    x += __builtin_amdgcn_update_dpp(0u, x, kRowBcast31, 0xC, 0xF, false);
+    return x;
+}
+
 }  // namespace rs
