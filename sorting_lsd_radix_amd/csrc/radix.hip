@@ -52,6 +52,17 @@ constexpr int kPassWavesPerSimd = 4;
 constexpr int kSortBlock = 1024;
 constexpr int kSortItems = 16;
 constexpr int kSortTile = kSortBlock * kSortItems;
+// Passes of at most this many tiles (of the 1024-thread shapes) use the wide
+// look-back: every earlier tile's count is read at once, in batches of
+// kWideBatch per thread, instead of a walk one batch of tiles at a time.
+constexpr uint32_t kWideMaxTiles = 256;
+constexpr int kWideBatch = 8;
+// The hybrid sort's top-digit pass: 8192-key tiles while they are at most
+// kWideMaxTiles, so a small input spreads over twice as many CUs as with the
+// 16384-key shape (measured faster at 2^20 pairs; 4096-key tiles were slower,
+// their wide look-backs being longer); 16384-key tiles above that.
+constexpr int kMsdItems = 8;
+constexpr int kMsdTile = kSortBlock * kMsdItems;
 // Large pair sorts: bigger tiles cut the per-tile work (scans, look-back,
 // tile hand-out) per key.  24 keys and values per thread from the size that
 // gives every CU a tile; 28 (32 spills) once there are at least 2^26 keys,
@@ -80,6 +91,7 @@ constexpr uint32_t kHybridMaxN = 3u << 20;
 constexpr int kBucketBlock = 1024;
 constexpr int kBucketItems = 16;
 constexpr uint32_t kBucketCap = kBucketBlock * kBucketItems;
+static_assert(kHybridMaxN / kSortTile <= kWideMaxTiles, "the multi-pass fallback uses the wide look-back");
 // Earlier tiles read per look-back batch.  A wave waits for every word of a
 // batch that any of its lanes still needs, so small batches win: 2 measured
 // best for the 16384-key tiles (8 is 2-4 % slower), 1 for the 24576-key pair
@@ -399,8 +411,14 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t k, uint32_t shift, uint32_
 // tiles the scheduler hands it.  Per tile: load, stable in-wave rank (LDS
 // atomics or ballots), tile counts and scans, decoupled look-back, re-layout
 // in digit order in LDS, scatter of each digit run.
+// WIDE (passes of few tiles, 1024 threads): a tile publishes only its own
+// counts, and its exclusive prefix is the sum of the counts of all earlier
+// tiles, read by four threads per digit in parallel.  When a pass's tiles
+// all start together (a small input), a walk that stops at the nearest
+// published prefix takes about tile/4 dependent round trips for the last
+// tiles, while the reads here are independent.
 template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XF_IN, bool XF_OUT, bool KEY64,
-          bool MULTI = false>
+          bool MULTI = false, bool WIDE = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
 void onesweep_kernel(PassArgs a) {
     using Key = typename std::conditional<KEY64, uint64_t, uint32_t>::type;
@@ -410,6 +428,7 @@ void onesweep_kernel(PassArgs a) {
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
     static_assert(TILE <= 32768, "16-bit positions");
     static_assert(ITEMS % 4 == 0, "digits are packed four per register");
+    static_assert(!WIDE || BLOCK == 4 * kRadix, "the wide look-back uses four threads per digit");
 
     // One staging buffer: the keys in digit order, then the values in digit order.
     __shared__ Key s_buf[TILE];
@@ -419,6 +438,7 @@ void onesweep_kernel(PassArgs a) {
     __shared__ uint32_t s_wsum[2][kRadix / kWave];
     __shared__ uint32_t s_next;
     __shared__ uint32_t s_crowded;   // a digit of this tile holds too many of its keys
+    __shared__ uint32_t s_part[WIDE ? 3 * kRadix : 1];   // wide look-back: partial sums of threads 256..1023
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
@@ -447,14 +467,21 @@ void onesweep_kernel(PassArgs a) {
         xf_out = XF_OUT && a.multi_passes == 1;
     }
 
+    // The first tile is taken while the counts load (a small sort's block
+    // often has only this tile); a launch the gate stops leaves its counter
+    // unused.
+    if (tid == 0) {
+        if constexpr (MULTI) s_next = fetch_add_agent(&a.multi_counter[0], 1u);
+        else s_next = next_chunked_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
+    }
+    // global digit count of this pass (thread d holds digit d), in flight
+    // together with the gate's counts
+    uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
     if (a.gate != 0) {   // uniform: a gated launch of the hybrid sort
         const uint32_t c = (tid < kRadix) ? a.gate_bins[tid] : 0u;
         const bool oversize = __syncthreads_or(c > a.gate_cap);
         if (oversize != (a.gate == 2)) return;
     }
-
-    // global digit count of this pass (thread d holds digit d)
-    uint32_t bin = (tid < kRadix) ? a.bins[tid] : 0u;
     // Same-address LDS atomics serialise, so the atomic rank below is used
     // while no digit holds more than a share 2^-atomic_limit_log2 of the
     // pass's keys, and for a tile only if the block's previous tile had no
@@ -467,13 +494,15 @@ void onesweep_kernel(PassArgs a) {
 #endif
     bool atomic_rank = spread;   // uniform
 
-    for (;;) {
-        // A tile is taken only when the block can start on it at once: the
-        // time from taking a tile to publishing its count delays every later
-        // tile's look-back.
+    for (bool first_tile = true;; first_tile = false) {
+        // After the first, a tile is taken only when the block can start on it
+        // at once: the time from taking a tile to publishing its count delays
+        // every later tile's look-back.
         if (tid == 0) {
-            if constexpr (MULTI) s_next = fetch_add_agent(&a.multi_counter[0], 1u);
-            else s_next = next_chunked_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
+            if (!first_tile) {
+                if constexpr (MULTI) s_next = fetch_add_agent(&a.multi_counter[0], 1u);
+                else s_next = next_chunked_tile(a.sched, a.groups, a.chunk_log2, group, tiles);
+            }
             s_crowded = 0u;   // the previous tile's readers all passed a barrier since
         }
         // Only this wave reads and writes its counters during the rank, and the
@@ -594,7 +623,7 @@ void onesweep_kernel(PassArgs a) {
         const uint32_t real = (tid == last_digit) ? count - pads : count;
         if (tid < kRadix)
             store_state(&states[tile * kRadix + tid],
-                        (tile == 0 ? kStatePrefix : kStateAggregate) | real);
+                        (tile == 0 && !WIDE ? kStatePrefix : kStateAggregate) | real);
 
         uint32_t inc_c = 0, inc_b = 0;
         if (tid < kRadix) {
@@ -629,7 +658,20 @@ void onesweep_kernel(PassArgs a) {
         // before this one, loaded together so their latencies overlap each
         // other and the work below.
         uint32_t lb[LOOKBACK];
-        if (tid < kRadix && tile > 0) {
+        // Wide look-back: thread (q, d) = (tid / 256, tid % 256) sums digit d's
+        // counts of the tiles q, q + 4, q + 8, ... below this one, kWideBatch
+        // of them per batch of loads; the first batch is in flight during the
+        // re-layout.
+        const uint32_t wd = tid % kRadix, wq = tid / kRadix;
+        uint32_t wl[WIDE ? kWideBatch : 1];
+        if constexpr (WIDE) {
+#pragma unroll
+            for (int b = 0; b < kWideBatch; ++b) {
+                const uint32_t t = wq + 4u * b;
+                wl[b] = (t < tile) ? load_state(&states[t * kRadix + wd]) : kStateAggregate;
+            }
+        }
+        if (!WIDE && tid < kRadix && tile > 0) {
 #pragma unroll
             for (int b = 0; b < LOOKBACK; ++b) {
                 const int32_t t = static_cast<int32_t>(tile) - 1 - b;
@@ -664,7 +706,39 @@ void onesweep_kernel(PassArgs a) {
         // until the first published inclusive prefix; states are read in
         // batches of LOOKBACK tiles.  Tile 0 always publishes a prefix, so the
         // walk ends at tile 0 at the latest and never reads below it.
-        if (tid < kRadix) {
+        if constexpr (WIDE) {
+            // every earlier tile publishes its counts right after its rank,
+            // which waits on nothing, and is taken by a running block
+            // eventually (the scheduler's progress argument), so no wait here
+            // is forever
+            uint32_t part = 0;
+            for (uint32_t first_t = wq;; first_t += 4u * kWideBatch) {
+#pragma unroll
+                for (int b = 0; b < kWideBatch; ++b) {
+                    const uint32_t t = first_t + 4u * b;
+                    uint32_t st = wl[b];
+                    while ((st & ~kStateCountMask) == 0u) {   // (t < tile here: others hold a flag)
+                        __builtin_amdgcn_s_sleep(1);
+                        st = load_state(&states[t * kRadix + wd]);
+                    }
+                    if (t < tile) part += st & kStateCountMask;
+                }
+                const uint32_t next_t = first_t + 4u * kWideBatch;
+                if (next_t >= tile) break;
+#pragma unroll
+                for (int b = 0; b < kWideBatch; ++b) {
+                    const uint32_t t = next_t + 4u * b;
+                    wl[b] = (t < tile) ? load_state(&states[t * kRadix + wd]) : kStateAggregate;
+                }
+            }
+            if (wq > 0) s_part[(wq - 1) * kRadix + wd] = part;
+            __syncthreads();
+            if (tid < kRadix) {
+                const uint32_t excl = part + s_part[tid] + s_part[kRadix + tid] + s_part[2 * kRadix + tid];
+                s_adjust[tid] = bin_start + excl - local_start;
+                if (a.next_states) a.next_states[tile * kRadix + tid] = 0u;
+            }
+        } else if (tid < kRadix) {
             uint32_t excl = 0;
             if (tile > 0) {
                 int32_t nearest = static_cast<int32_t>(tile) - 1;   // tile of lb[0]
@@ -931,30 +1005,25 @@ __global__ __launch_bounds__(kBucketBlock) void bucket_sort_kernel(BucketArgs a)
     __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
     __shared__ uint32_t s_off[WAVES * kRadix];
     __shared__ uint32_t s_wsum[kRadix / kWave];
-    __shared__ uint32_t s_start;
+    __shared__ uint32_t s_count;
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
     const uint32_t wave = tid / kWave;
     const uint32_t b = blockIdx.x;
 
+    // Thread d < 256 holds bucket d's count; one load serves the gate, the
+    // bucket's start (the counts of the buckets below b, summed per wave) and
+    // its size.
     const uint32_t cd = (tid < kRadix) ? a.top_bins[tid] : 0u;
+    const uint32_t below = wave_inclusive_sum_dpp(tid < b ? cd : 0u);
+    if (wave < kRadix / kWave && lane == kWave - 1) s_wsum[wave] = below;
+    if (tid == b) s_count = cd;
     if (__syncthreads_or(cd > a.cap)) return;   // uniform: the LSD passes sort this input
-    if (wave == 0) {
-        // keys in the buckets below b: lane l adds the counts of buckets 4l .. 4l+3
-        uint32_t below = 0;
+    uint32_t start = 0;
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const uint32_t d = lane * 4 + i;
-            if (d < b) below += a.top_bins[d];
-        }
-#pragma unroll
-        for (int off = 32; off > 0; off >>= 1) below += __shfl_xor(below, off, kWave);
-        if (lane == 0) s_start = below;
-    }
-    __syncthreads();
-    const uint32_t start = s_start;
-    const uint32_t c = a.top_bins[b];
+    for (int w = 0; w < kRadix / kWave; ++w) start += s_wsum[w];
+    const uint32_t c = s_count;
     if (c == 0) return;   // uniform
     const uint32_t rows = (c + BLOCK - 1) / BLOCK;
     const uint32_t first = wave * (kWave * rows) + lane;   // row j of this lane: first + 64 j
@@ -1061,6 +1130,7 @@ struct SortLayout {
     size_t bins, sched, multi, states0, states_m, states1, tmp_keys, tmp_vals, tmp_keys2, total;
     uint64_t clear_words;
     uint32_t tiles;
+    uint32_t msd_tiles;   // tiles of the hybrid sort's top-digit pass (states0 holds its states)
 };
 
 constexpr uint32_t kSchedWords = 64;           // per pass: kGroups counters, padded to 256 bytes
@@ -1095,6 +1165,12 @@ bool hybrid_size(uint64_t n, const SortKind& kind) {
     return !kind.key64 && n > kTileSortMax && n <= kHybridMaxN;
 }
 
+// Keys per tile of the hybrid sort's top-digit pass.
+uint32_t msd_tile_keys(uint64_t n) {
+    return (n + kMsdTile - 1) / kMsdTile <= kWideMaxTiles ? static_cast<uint32_t>(kMsdTile)
+                                                           : static_cast<uint32_t>(kSortTile);
+}
+
 SortLayout sort_layout(uint64_t n, bool pairs, const SortKind& kind) {
     SortLayout L{};
     const int max_passes = kind.key64 ? kMaxPasses64 : kMaxPasses;
@@ -1102,6 +1178,14 @@ SortLayout sort_layout(uint64_t n, bool pairs, const SortKind& kind) {
     const uint64_t tile_keys = pass_tile_keys(n, pairs, kind.key64);
     L.tiles = static_cast<uint32_t>((n + tile_keys - 1) / tile_keys);
     const size_t states_bytes = align_up(static_cast<size_t>(L.tiles) * kRadix * 4);
+    L.msd_tiles = 0;
+    size_t states0_bytes = states_bytes;
+    if (hybrid_size(n, kind)) {
+        const uint32_t mt = msd_tile_keys(n);
+        L.msd_tiles = static_cast<uint32_t>((n + mt - 1) / mt);
+        const size_t b = align_up(static_cast<size_t>(L.msd_tiles) * kRadix * 4);
+        if (b > states0_bytes) states0_bytes = b;
+    }
     size_t off = 0;
     L.bins = off;
     off += align_up(static_cast<size_t>(max_passes) * kRadix * 4);
@@ -1110,7 +1194,7 @@ SortLayout sort_layout(uint64_t n, bool pairs, const SortKind& kind) {
     L.multi = off;
     off += kSchedWords * 4;
     L.states0 = off;
-    off += states_bytes;
+    off += states0_bytes;
     L.states_m = off;
     if (hybrid_size(n, kind)) off += static_cast<size_t>(kMaxPasses) * states_bytes;
     L.clear_words = off / 4;
@@ -1137,9 +1221,9 @@ uint32_t resident_blocks(K kernel, int block) {
     return r < kMaxResidentBlocks ? r : kMaxResidentBlocks;
 }
 
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XI, bool XO, bool KEY64>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XI, bool XO, bool KEY64, bool WIDE>
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
-    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, XI, XO, KEY64>;
+    auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, XI, XO, KEY64, false, WIDE>;
     static const uint32_t resident = resident_blocks(kern, BLOCK);   // one-time init
     const TileGrid g = tile_grid(a.tiles, resident);
     PassArgs b = a;
@@ -1149,18 +1233,19 @@ hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     return hipGetLastError();
 }
 
-template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool KEY64 = false>
+template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool KEY64 = false, bool WIDE = false>
 hipError_t launch_pass_items(bool xf_in, bool xf_out, const PassArgs& a, hipStream_t s) {
-    if (xf_in && xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, true, KEY64>(a, s);
-    if (xf_in) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, false, KEY64>(a, s);
-    if (xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, true, KEY64>(a, s);
-    return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false, KEY64>(a, s);
+    if (xf_in && xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, true, KEY64, WIDE>(a, s);
+    if (xf_in) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, true, false, KEY64, WIDE>(a, s);
+    if (xf_out) return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, true, KEY64, WIDE>(a, s);
+    return launch_pass_t<BLOCK, ITEMS, LOOKBACK, PAIRS, false, false, KEY64, WIDE>(a, s);
 }
 
-// The hybrid sort's fallback: every LSD pass in one launch of the small shape.
+// The hybrid sort's fallback: every LSD pass in one launch of the small shape
+// (hybrid sizes have at most kHybridMaxN / kSortTile <= kWideMaxTiles tiles).
 template <bool PAIRS, bool XF>
 hipError_t launch_multi_t(const PassArgs& a, hipStream_t s) {
-    auto kern = onesweep_kernel<kSortBlock, kSortItems, kSortLookback, PAIRS, XF, XF, false, true>;
+    auto kern = onesweep_kernel<kSortBlock, kSortItems, kSortLookback, PAIRS, XF, XF, false, true, true>;
     static const uint32_t resident = resident_blocks(kern, kSortBlock);   // one-time init
     const uint32_t grid = a.tiles < resident ? a.tiles : resident;
     PassArgs b = a;
@@ -1192,7 +1277,20 @@ hipError_t launch_pass(bool xf_in, bool xf_out, bool key64, const PassArgs& a, h
             return launch_pass_items<kKeysBlock, kKeysItems, kSortLookback, false>(xf_in, xf_out, a, s);
         }
     }
+    if (a.tiles <= kWideMaxTiles)
+        return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS, false, true>(xf_in, xf_out, a, s);
     return launch_pass_items<kSortBlock, kSortItems, kSortLookback, PAIRS>(xf_in, xf_out, a, s);
+}
+
+// The hybrid sort's top-digit pass (the wide look-back; the tile size is
+// chosen by msd_tile_keys, and a.tiles is the tile count for it).
+hipError_t launch_msd_pass(bool pairs, bool xf_in, const PassArgs& a, hipStream_t s) {
+    if (msd_tile_keys(a.n) == static_cast<uint32_t>(kMsdTile)) {
+        return pairs ? launch_pass_items<kSortBlock, kMsdItems, kSortLookback, true, false, true>(xf_in, false, a, s)
+                     : launch_pass_items<kSortBlock, kMsdItems, kSortLookback, false, false, true>(xf_in, false, a, s);
+    }
+    return pairs ? launch_pass_items<kSortBlock, kSortItems, kSortLookback, true, false, true>(xf_in, false, a, s)
+                 : launch_pass_items<kSortBlock, kSortItems, kSortLookback, false, false, true>(xf_in, false, a, s);
 }
 
 template <int BLOCK, int ITEMS, bool PAIRS>
@@ -1378,7 +1476,7 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
         a.dst_keys = tmp_keys;
         a.dst_vals = pairs ? tmp_vals : nullptr;
         a.n = n;
-        a.tiles = L.tiles;
+        a.tiles = L.msd_tiles;
         a.shift = pd.shift[top];
         a.width = pd.width[top];
         a.bins = bins + top * kRadix;
@@ -1391,8 +1489,7 @@ hipError_t launch_sort(const SortIo& io, const SortKind& kind, int begin_bit, in
         a.gate_cap = kBucketCap;
         a.gate_bins = bins + top * kRadix;
         timing_before(stream, RS_KERNEL_ONESWEEP);
-        e = pairs ? launch_pass<true>(kind.transforms, false, false, a, stream)
-                  : launch_pass<false>(kind.transforms, false, false, a, stream);
+        e = launch_msd_pass(pairs, kind.transforms, a, stream);
         timing_after(stream);
         if (e != hipSuccess) return e;
 

@@ -57,8 +57,10 @@ def test_bucket_sizes_on_row_edges_and_empty_buckets():
     check(with_bucket_sizes(sizes, 3))
 
 
-@pytest.mark.parametrize("n", [CAP + 1, 100000, (1 << 20) + 17, (2 << 20) + 1, HYBRID_MAX,
-                               HYBRID_MAX + 1])
+# the top-digit pass uses 8192-key tiles up to 256 of them (n <= 2^21) and
+# 16384-key tiles above
+@pytest.mark.parametrize("n", [CAP + 1, 100000, (1 << 20) + 17, (2 << 20) - 1, 2 << 20, (2 << 20) + 1,
+                               HYBRID_MAX, HYBRID_MAX + 1])
 def test_uniform_sizes(n):
     print("hybrid: uniform n=%d" % n, flush=True)
     check(rng(n).integers(0, 2**32, n, dtype=np.uint32))
