@@ -17,7 +17,7 @@ import sorting_lsd_radix_amd as rs
 
 MAX_N = 1 << 30
 WINDOW = 2 * 28672
-FIXED = 4 * 256 * 4 + 4 * 64 * 4      # digit counts + tile counters of four passes
+FIXED = 4 * 256 * 4 + 4 * 64 * 4 + 64 * 4   # digit counts + tile counters of four passes + multi-pass counters
 
 
 def align256(x):
