@@ -148,20 +148,32 @@ struct PassDigits {
     KeyXform xf;   // applied to each key before its digits are counted (XF kernels)
 };
 
-template <bool XF>
+// PASSES digits of one key counted (one bit-field extract each; the pass
+// count is a template argument, so no per-digit branch).
+template <bool XF, int PASSES>
 __device__ __forceinline__ void count_key(uint32_t* s_hist, uint32_t key, const PassDigits& pd,
                                           uint32_t sub) {
     if (XF) key = xform32(key, pd.xf);
 #pragma unroll
-    for (int p = 0; p < kMaxPasses; ++p) {
-        if (p < static_cast<int>(pd.passes)) {
-            const uint32_t d = (key >> pd.shift[p]) & pd.mask[p];
-            atomicAdd(&s_hist[(p * kRadix + d) * kUpSub + sub], 1u);
-        }
+    for (int p = 0; p < PASSES; ++p) {
+        const uint32_t d = __builtin_amdgcn_ubfe(key, pd.shift[p], pd.width[p]);
+        atomicAdd(&s_hist[(p * kRadix + d) * kUpSub + sub], 1u);
     }
 }
 
-template <bool XF>
+template <bool XF, int PASSES>
+__device__ __forceinline__ void count_rows4(uint32_t* s_hist, const u32x4 (&q)[4], const PassDigits& pd,
+                                            uint32_t sub) {
+#pragma unroll
+    for (int u = 0; u < 4; ++u) {
+        count_key<XF, PASSES>(s_hist, q[u].x, pd, sub);
+        count_key<XF, PASSES>(s_hist, q[u].y, pd, sub);
+        count_key<XF, PASSES>(s_hist, q[u].z, pd, sub);
+        count_key<XF, PASSES>(s_hist, q[u].w, pd, sub);
+    }
+}
+
+template <bool XF, int PASSES>
 __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __restrict__ keys,
                                                            uint32_t n, PassDigits pd,
                                                            uint32_t* __restrict__ bins) {
@@ -183,28 +195,22 @@ __global__ __launch_bounds__(kUpBlock) void upsweep_kernel(const uint32_t* __res
         u32x4 q[4];
 #pragma unroll
         for (int u = 0; u < 4; ++u) q[u] = __builtin_nontemporal_load(&k4[i + u * kUpBlock]);
-#pragma unroll
-        for (int u = 0; u < 4; ++u) {
-            count_key<XF>(s_hist, q[u].x, pd, sub);
-            count_key<XF>(s_hist, q[u].y, pd, sub);
-            count_key<XF>(s_hist, q[u].z, pd, sub);
-            count_key<XF>(s_hist, q[u].w, pd, sub);
-        }
+        count_rows4<XF, PASSES>(s_hist, q, pd, sub);
     }
     for (; i < end; i += kUpBlock) {
-        const u32x4 q = __builtin_nontemporal_load(&k4[i]);
-        count_key<XF>(s_hist, q.x, pd, sub);
-        count_key<XF>(s_hist, q.y, pd, sub);
-        count_key<XF>(s_hist, q.z, pd, sub);
-        count_key<XF>(s_hist, q.w, pd, sub);
+        const u32x4 v = __builtin_nontemporal_load(&k4[i]);
+        count_key<XF, PASSES>(s_hist, v.x, pd, sub);
+        count_key<XF, PASSES>(s_hist, v.y, pd, sub);
+        count_key<XF, PASSES>(s_hist, v.z, pd, sub);
+        count_key<XF, PASSES>(s_hist, v.w, pd, sub);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * 4)
-        count_key<XF>(s_hist, keys[nvec * 4 + threadIdx.x], pd, sub);
+        count_key<XF, PASSES>(s_hist, keys[nvec * 4 + threadIdx.x], pd, sub);
     __syncthreads();
 
     // Thread i sums bin i's sub-histograms starting at sub i mod 32, so the
     // lanes of one read hit different banks.
-    for (uint32_t i = threadIdx.x; i < pd.passes * kRadix; i += kUpBlock) {
+    for (uint32_t i = threadIdx.x; i < PASSES * kRadix; i += kUpBlock) {
         uint32_t c = 0;
 #pragma unroll
         for (int s = 0; s < kUpSub; ++s) c += s_hist[i * kUpSub + ((i + s) % kUpSub)];
@@ -1325,6 +1331,17 @@ int upsweep_grid(uint32_t n) {
     return static_cast<int>(g);
 }
 
+template <bool XF>
+void launch_upsweep32(const uint32_t* keys, uint32_t n, const PassDigits& pd, uint32_t* bins, int grid,
+                      hipStream_t s) {
+    switch (pd.passes) {
+    case 1: upsweep_kernel<XF, 1><<<grid, kUpBlock, 0, s>>>(keys, n, pd, bins); break;
+    case 2: upsweep_kernel<XF, 2><<<grid, kUpBlock, 0, s>>>(keys, n, pd, bins); break;
+    case 3: upsweep_kernel<XF, 3><<<grid, kUpBlock, 0, s>>>(keys, n, pd, bins); break;
+    default: upsweep_kernel<XF, 4><<<grid, kUpBlock, 0, s>>>(keys, n, pd, bins); break;
+    }
+}
+
 // Digit positions of every pass over [begin_bit, end_bit), and the forward transform.
 PassDigits pass_digits(int begin_bit, int end_bit, const KeyXform& xf) {
     PassDigits pd{};
@@ -1356,8 +1373,8 @@ hipError_t launch_upsweep(const SortIo& io, const SortKind& kind, const PassDigi
             else upsweep64_kernel<false, false><<<grid, kUpBlock, 0, stream>>>(io.keys_in, nullptr, n, pd, bins);
         }
     } else {
-        if (xf) upsweep_kernel<true><<<grid, kUpBlock, 0, stream>>>(io.keys_in, n, pd, bins);
-        else upsweep_kernel<false><<<grid, kUpBlock, 0, stream>>>(io.keys_in, n, pd, bins);
+        if (xf) launch_upsweep32<true>(io.keys_in, n, pd, bins, grid, stream);
+        else launch_upsweep32<false>(io.keys_in, n, pd, bins, grid, stream);
     }
     const hipError_t e = hipGetLastError();
     timing_after(stream);
