@@ -283,6 +283,30 @@ def keys_only_companion(kin, n, steps, warmup, stream, pairs_keys_out, check):
             "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()}}
 
 
+def roofline_terms(kind, n, b, e):
+    """(dominant kernel, algorithmic bytes per element of one launch of it,
+    algorithmic bytes of the whole step) for a workload."""
+    passes = (e - b + 7) // 8
+    if kind in ("compact", "bitonic", "scan"):
+        # read every element once, write every output element once
+        return {"compact": "compact", "bitonic": "bitonic", "scan": "scan"}[kind], 8, 8 * n
+    if kind == "partition":
+        # read and write every element and its value once (the counting read is an overhead)
+        return "select", 16, 16 * n
+    if kind == "pairs_u64":
+        # 8-byte key + 4-byte value, read and written by every pass
+        return "onesweep", 24, 24 * n * passes
+    bytes_per = 8 if kind == "keys_u32" else 16
+    if n <= TILE_SORT_MAX:
+        # the whole sort in one workgroup: the keys (and values) cross HBM once each way
+        return "tile_sort", bytes_per, bytes_per * n
+    if n <= HYBRID_MAX and passes >= 2:
+        # hybrid: the bucket sort (one read and one write of every key and value)
+        # after the top digit's pass; the metric still counts every pass's bytes
+        return "bucket_sort", bytes_per, bytes_per * n * passes
+    return "onesweep", bytes_per, bytes_per * n * passes
+
+
 def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
     import numpy as np
     import torch
@@ -361,34 +385,7 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
             sys.exit(1)
         print("bench: output check ok", file=sys.stderr, flush=True)
 
-    passes = (e - b + 7) // 8
-    if kind in ("compact", "bitonic", "scan"):
-        # read every element once, write every output element once
-        dom, bytes_per = {"compact": "compact", "bitonic": "bitonic", "scan": "scan"}[kind], 8
-        algo_total = 8 * n
-    elif kind == "partition":
-        # read and write every element and its value once (the counting read is an overhead)
-        dom, bytes_per = "select", 16
-        algo_total = 16 * n
-    elif kind == "pairs_u64":
-        # 8-byte key + 4-byte value, read and written by every pass
-        dom, bytes_per = "onesweep", 24
-        algo_total = 24 * n * passes
-    elif n <= TILE_SORT_MAX:
-        # the whole sort in one workgroup: the keys (and values) cross HBM once each way
-        dom = "tile_sort"
-        bytes_per = 8 if kind == "keys_u32" else 16
-        algo_total = bytes_per * n
-    elif n <= HYBRID_MAX and passes >= 2:
-        # hybrid: the bucket sort (one read and one write of every key and value)
-        # after the top digit's pass; the metric still counts every pass's bytes
-        dom = "bucket_sort"
-        bytes_per = 8 if kind == "keys_u32" else 16
-        algo_total = bytes_per * n * passes
-    else:
-        dom = "onesweep"
-        bytes_per = 8 if kind == "keys_u32" else 16
-        algo_total = bytes_per * n * passes
+    dom, bytes_per, algo_total = roofline_terms(kind, n, b, e)
     dom_ms = per_kernel.get(dom, [float("nan")])
     dom_ms = sum(dom_ms) / len(dom_ms)
     algo_bytes = bytes_per * n
@@ -436,7 +433,7 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
                   "pairs_u64": "u64 keys, u32 values"}[kind],
         "data": "synthetic",
         "config": {"workload": desc, "n": n, "begin_bit": b, "end_bit": e,
-                   "passes": passes if kind not in ("compact", "bitonic", "scan", "partition")
+                   "passes": (e - b + 7) // 8 if kind not in ("compact", "bitonic", "scan", "partition")
                    else None},
         "roofline": {"bound": "hbm", "achieved": round(achieved, 1), "peak": HBM_PEAK_GBS,
                      "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBS, 4), "traffic": traffic,
@@ -455,7 +452,7 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
 
 KERNEL_MATCH = {"onesweep": "onesweep_kernel", "upsweep": "upsweep_kernel",
                 "compact": "compact_kernel", "tile_sort": "tile_sort_kernel",
-                "bucket_sort": "bucket_sort_kernel",
+                "bucket_sort": "bucket_sort_kernel", "scan": "scan_kernel", "select": "select_kernel",
                 "bitonic": "bitonic_tile_kernel", "copy": "__amd_rocclr_copyBuffer"}
 COPY_BYTES = 4 << 28   # the --copy-calibration copy moves 1 GiB each way
 
@@ -478,10 +475,7 @@ def record_traffic(name, fetch_dir, write_dir):
 
     fetch, write = per_kernel(fetch_dir), per_kernel(write_dir)
     desc, kind, n, b, e = WORKLOADS[name]
-    dom = ("compact" if kind == "compact" else "bitonic" if kind == "bitonic"
-           else "tile_sort" if n <= TILE_SORT_MAX
-           else "bucket_sort" if n <= HYBRID_MAX and (e - b) > 8 else "onesweep")
-    bytes_per = 8 if kind in ("keys_u32", "compact", "bitonic") else 16
+    dom, bytes_per, _ = roofline_terms(kind, n, b, e)
     f_factor = COPY_BYTES / (fetch["copy"] * 1024)
     w_factor = COPY_BYTES / (write["copy"] * 1024)
     entry = {

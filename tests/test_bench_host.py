@@ -98,3 +98,29 @@ def test_output_checks_accept_correct_and_reject_broken_outputs():
     f = rng.standard_normal(n).astype(np.float32)
     fo = np.argsort(bench.f32_order(f.view(np.uint32)), kind="stable").astype(np.uint32)
     assert bench.check_output("pairs_f32", f.view(np.uint32), vals, f[fo], fo, 0, 0, 32)
+
+
+def test_bench_functions_read_only_defined_names():
+    """Every name a function of bench.py reads without assigning it is a
+    module-level name or a builtin (the GPU-only code paths of the bench run
+    on the GPU only, so a stray name there would otherwise surface there)."""
+    import builtins
+    import symtable
+
+    import bench
+    with open(bench.__file__) as f:
+        top = symtable.symtable(f.read(), bench.__file__, "exec")
+    missing = []
+
+    def walk(table):
+        for child in table.get_children():
+            if child.get_type() == "function":
+                for sym in child.get_symbols():
+                    name = sym.get_name()
+                    if (sym.is_referenced() and sym.is_global() and not hasattr(bench, name)
+                            and not hasattr(builtins, name)):
+                        missing.append((child.get_name(), name))
+            walk(child)
+
+    walk(top)
+    assert not missing, missing
