@@ -443,8 +443,9 @@ def run_workload(name, steps, warmup, check, with_cpu, copy_calibration=False):
         "whole_step_roofline_frac": round(algo_total / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
         "kernel_ms": {k: round(sum(v) / len(v), 5) for k, v in per_kernel.items()},
     }
-    if name == DEFAULT:
+    if name == DEFAULT and not copy_calibration:
         # the metric names keys-only sorts as well: same keys, same step count
+        # (not in the counter runs, whose per-kernel means would mix the two sorts' passes)
         result["keys_u32_2p28"] = keys_only_companion(kin, n, steps, warmup, stream, kout, check)
     result["cpu_baseline"] = cpu_baseline(name, keys, vals) if with_cpu else None
     return result
