@@ -692,19 +692,33 @@ void onesweep_kernel(PassArgs a) {
         if constexpr (PAIRS) load_rows<ITEMS, TILE>(src_vals, tile, n, wave, lane, v);
 
         // ---- re-lay the keys out in digit order in LDS ---------------------------
+        // Keys-only passes go in groups of RG rows: the group's digit-offset
+        // reads are issued together, then its stores, so the reads' LDS
+        // latencies overlap instead of each store waiting on its own read
+        // (2^28 keys-only pass 0.501 -> 0.488 ms; pair passes, whose tiles
+        // wait on memory, gained nothing and keep one row at a time).
+        constexpr int RG = PAIRS ? 1 : (ITEMS % 8 == 0 ? 8 : 4);
 #pragma unroll
-        for (int j = 0; j < ITEMS; ++j) {
-            // recompute the digit rather than keep the rank loop's LDS addresses
-            // alive across the scans (an empty asm hides the reuse)
-            Key key = k[j];
-            asm volatile("" : "+v"(key));
-            const uint32_t d = digit_of(key, shift, width);
-            // (the clamp never changes a consistent position; it keeps the store in the tile)
-            const uint32_t sh = 16 * (j % 2);
-            const uint32_t p = min(s_off[wave * kRadix + d] + ((pos[j / 2] >> sh) & 0xFFFFu),
-                                   static_cast<uint32_t>(TILE - 1));
-            pos[j / 2] = (pos[j / 2] & ~(0xFFFFu << sh)) | (p << sh);
-            s_buf[p] = key;
+        for (int g = 0; g < ITEMS; g += RG) {
+            Key key[RG];
+            uint32_t base[RG];
+#pragma unroll
+            for (int i = 0; i < RG; ++i) {
+                // recompute the digit rather than keep the rank loop's LDS addresses
+                // alive across the scans (an empty asm hides the reuse)
+                key[i] = k[g + i];
+                asm volatile("" : "+v"(key[i]));
+                base[i] = s_off[wave * kRadix + digit_of(key[i], shift, width)];
+            }
+#pragma unroll
+            for (int i = 0; i < RG; ++i) {
+                const int j = g + i;
+                // (the clamp never changes a consistent position; it keeps the store in the tile)
+                const uint32_t sh = 16 * (j % 2);
+                const uint32_t p = min(base[i] + ((pos[j / 2] >> sh) & 0xFFFFu), static_cast<uint32_t>(TILE - 1));
+                pos[j / 2] = (pos[j / 2] & ~(0xFFFFu << sh)) | (p << sh);
+                s_buf[p] = key[i];
+            }
         }
 
         // ---- decoupled look-back: same-digit keys in all earlier tiles --------
