@@ -1,9 +1,11 @@
 """GPU check of the hardware property the stable rank of the sort relies on.
 
-Every one-sweep pass kernel (keys only and key-value, every tile shape, u32
-and float keys) ranks a key with one LDS atomic add (`ds_add_rtn_u32`) on its
+Every one-sweep pass kernel (keys only and key-value, every tile shape and
+key type, the hybrid sort's top-digit pass and its multi-pass fallback
+included) ranks a key with one LDS atomic add (`ds_add_rtn_u32`) on its
 wave's digit counter while the digits of the pass are spread out, and the
-one-workgroup sort of up to 16384 keys always does.  That rank is the stable
+one-workgroup sort of up to 16384 keys and the hybrid sort's per-bucket sort
+always do.  That rank is the stable
 one only if the lanes of one instruction that hit the same counter are
 served in lane order: observed gfx950 behaviour, not a documented guarantee.
 This test runs a probe kernel (tests/hw_probe/lds_lane_order.hip) that
