@@ -99,8 +99,10 @@ __device__ __forceinline__ uint64_t xform64(uint64_t k, const KeyXform& x) {
     return k ^ ((static_cast<uint64_t>(mh) << 32) | ml);
 }
 
-// Inclusive sum over the 64 lanes of a wave.
-__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
+// The same sum with LDS-crossbar shuffles (six dependent ds_bpermute steps);
+// slower on its own, but the one-sweep pair passes, which sit at the edge of
+// their register budget, run faster with it than with the DPP form.
+__device__ __forceinline__ uint32_t wave_inclusive_sum_shfl(uint32_t x) {
     const uint32_t lane = lane_id();
 #pragma unroll
     for (int off = 1; off < kWave; off <<= 1) {
@@ -110,11 +112,11 @@ __device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     return x;
 }
 
-// Inclusive sum over the 64 lanes of a wave with DPP moves instead of LDS
-// crossbar shuffles: a Hillis-Steele scan inside each row of 16 lanes
-// (shifts by 1, 2, 4, 8, zeros shifted in), then row 15's total broadcast into
-// rows 1 and 3 and lane 31's into rows 2 and 3.
-__device__ __forceinline__ uint32_t wave_inclusive_sum_dpp(uint32_t x) {
+// Inclusive sum over the 64 lanes of a wave (all 64 lanes active), with DPP
+// moves instead of LDS crossbar shuffles: a Hillis-Steele scan inside each row
+// of 16 lanes (shifts by 1, 2, 4, 8, zeros shifted in), then row 15's total
+// broadcast into rows 1 and 3 and lane 31's into rows 2 and 3.
+__device__ __forceinline__ uint32_t wave_inclusive_sum(uint32_t x) {
     constexpr int kRowShr = 0x110;      // row_shr:n is kRowShr + n
     constexpr int kRowBcast15 = 0x142;
     constexpr int kRowBcast31 = 0x143;

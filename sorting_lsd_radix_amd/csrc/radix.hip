@@ -633,8 +633,8 @@ void onesweep_kernel(PassArgs a) {
 
         uint32_t inc_c = 0, inc_b = 0;
         if (tid < kRadix) {
-            inc_c = wave_inclusive_sum(count);
-            inc_b = wave_inclusive_sum(bin);
+            inc_c = PAIRS ? wave_inclusive_sum_shfl(count) : wave_inclusive_sum(count);
+            inc_b = PAIRS ? wave_inclusive_sum_shfl(bin) : wave_inclusive_sum(bin);
             if (lane == kWave - 1) {
                 s_wsum[0][wave] = inc_c;
                 s_wsum[1][wave] = inc_b;
@@ -890,8 +890,10 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
     static_assert(BLOCK >= kRadix && BLOCK % kWave == 0, "one thread per digit needed");
     static_assert(TILE <= 32768 && ITEMS % 2 == 0, "16-bit positions, two per register");
 
-    __shared__ uint32_t s_keys[TILE];
-    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    // the tile in digit order: keys, or (PAIRS) key and value in one 8-byte
+    // word, so each slot takes one LDS write and one read per pass
+    __shared__ uint32_t s_keys[PAIRS ? 1 : TILE];
+    __shared__ uint64_t s_kv[PAIRS ? TILE : 1];
     __shared__ uint32_t s_off[WAVES * kRadix];   // per-wave digit counters, then offsets
     __shared__ uint32_t s_wsum[kRadix / kWave];
 
@@ -968,16 +970,21 @@ __global__ __launch_bounds__(BLOCK) void tile_sort_kernel(const uint32_t* __rest
             const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
             const uint32_t q = (s_off[wave * kRadix + d] + ((pos[j / 2] >> (16 * (j % 2))) & 0xFFFFu)) &
                                (TILE - 1);
-            s_keys[q] = k[j];
-            if constexpr (PAIRS) s_vals[q] = v[j];
+            if constexpr (PAIRS) s_kv[q] = (static_cast<uint64_t>(v[j]) << 32) | k[j];
+            else s_keys[q] = k[j];
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
-            k[j] = s_keys[first + j * kWave];
-            if constexpr (PAIRS) v[j] = s_vals[first + j * kWave];
+            if constexpr (PAIRS) {
+                const uint64_t kv = s_kv[first + j * kWave];
+                k[j] = static_cast<uint32_t>(kv);
+                v[j] = static_cast<uint32_t>(kv >> 32);
+            } else {
+                k[j] = s_keys[first + j * kWave];
+            }
         }
-        // the next pass writes s_keys and s_vals only after two more barriers
+        // the next pass writes the staging buffer only after two more barriers
     }
 
 #pragma unroll
@@ -1021,8 +1028,10 @@ __global__ __launch_bounds__(kBucketBlock) void bucket_sort_kernel(BucketArgs a)
     constexpr int TILE = BLOCK * ITEMS;
     static_assert((TILE & (TILE - 1)) == 0, "positions are masked to the tile");
 
-    __shared__ uint32_t s_keys[TILE];
-    __shared__ uint32_t s_vals[PAIRS ? TILE : 1];
+    // the tile in digit order: keys, or (PAIRS) key and value in one 8-byte
+    // word, so each slot takes one LDS write and one read per pass
+    __shared__ uint32_t s_keys[PAIRS ? 1 : TILE];
+    __shared__ uint64_t s_kv[PAIRS ? TILE : 1];
     __shared__ uint32_t s_off[WAVES * kRadix];
     __shared__ uint32_t s_wsum[kRadix / kWave];
     __shared__ uint32_t s_count;
@@ -1036,7 +1045,7 @@ __global__ __launch_bounds__(kBucketBlock) void bucket_sort_kernel(BucketArgs a)
     // bucket's start (the counts of the buckets below b, summed per wave) and
     // its size.
     const uint32_t cd = (tid < kRadix) ? a.top_bins[tid] : 0u;
-    const uint32_t below = wave_inclusive_sum_dpp(tid < b ? cd : 0u);
+    const uint32_t below = wave_inclusive_sum(tid < b ? cd : 0u);
     if (wave < kRadix / kWave && lane == kWave - 1) s_wsum[wave] = below;
     if (tid == b) s_count = cd;
     if (__syncthreads_or(cd > a.cap)) return;   // uniform: the LSD passes sort this input
@@ -1108,16 +1117,21 @@ __global__ __launch_bounds__(kBucketBlock) void bucket_sort_kernel(BucketArgs a)
             if (j < static_cast<int>(rows)) {
                 const uint32_t d = __builtin_amdgcn_ubfe(k[j], shift, width);
                 const uint32_t q = (s_off[wave * kRadix + d] + pos[j]) & (TILE - 1);
-                s_keys[q] = k[j];
-                if constexpr (PAIRS) s_vals[q] = v[j];
+                if constexpr (PAIRS) s_kv[q] = (static_cast<uint64_t>(v[j]) << 32) | k[j];
+                else s_keys[q] = k[j];
             }
         }
         __syncthreads();
 #pragma unroll
         for (int j = 0; j < ITEMS; ++j) {
             if (j < static_cast<int>(rows)) {
-                k[j] = s_keys[first + j * kWave];
-                if constexpr (PAIRS) v[j] = s_vals[first + j * kWave];
+                if constexpr (PAIRS) {
+                    const uint64_t kv = s_kv[first + j * kWave];
+                    k[j] = static_cast<uint32_t>(kv);
+                    v[j] = static_cast<uint32_t>(kv >> 32);
+                } else {
+                    k[j] = s_keys[first + j * kWave];
+                }
             }
         }
         // the next pass writes the staging buffers only after two more barriers

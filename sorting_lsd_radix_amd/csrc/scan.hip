@@ -132,7 +132,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
             x[q][1] += x[q][0];
             x[q][2] += x[q][1];
             x[q][3] += x[q][2];
-            const uint32_t inc = wave_inclusive_sum_dpp(x[q][3]);
+            const uint32_t inc = wave_inclusive_sum(x[q][3]);
             wave_excl[q] = inc - x[q][3];
             if (lane == kWave - 1) s_part[q * WAVES + wave] = inc;
         }
@@ -144,7 +144,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
 #pragma unroll
             for (int g = 0; g < PARTS / kWave; ++g) {
                 const uint32_t v = s_part[g * kWave + lane];
-                const uint32_t inc = wave_inclusive_sum_dpp(v);
+                const uint32_t inc = wave_inclusive_sum(v);
                 s_part[g * kWave + lane] = carry + inc - v;
                 carry += __shfl(inc, kWave - 1, kWave);
             }
