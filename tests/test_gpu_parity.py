@@ -92,8 +92,10 @@ def dist_keys(kind, n):
     return r.integers(0, 256, n, dtype=np.uint32) << np.uint32(24)
 
 
+# LARGE - 17: 256 tiles of 16384 keys, the largest LSD sort whose passes use
+# the wide look-back; LARGE + 1234: 257 tiles, the walk
 @pytest.mark.parametrize("kind", DISTRIBUTIONS)
-@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE + 1234, PLARGE + 1234])
+@pytest.mark.parametrize("n", [2000, 3 * TILE + 1234, LARGE - 17, LARGE + 1234, PLARGE + 1234])
 def test_pairs_u32_distributions(kind, n):
     keys = dist_keys(kind, n)
     print("pairs u32 distribution=%s n=%d" % (kind, n), flush=True)
