@@ -421,8 +421,10 @@ __device__ __forceinline__ uint32_t digit_of(uint64_t k, uint32_t shift, uint32_
 // counts, and its exclusive prefix is the sum of the counts of all earlier
 // tiles, read by four threads per digit in parallel.  When a pass's tiles
 // all start together (a small input), a walk that stops at the nearest
-// published prefix takes about tile/4 dependent round trips for the last
-// tiles, while the reads here are independent.
+// published prefix can take up to about tile/4 dependent round trips for the
+// last tiles, while the reads here are independent.  (At 64 tiles both forms
+// measured the same; the wide one is what lets the hybrid sort's top-digit
+// pass use 128 tiles of 8192 keys.)
 template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XF_IN, bool XF_OUT, bool KEY64,
           bool MULTI = false, bool WIDE = false>
 __global__ __launch_bounds__(BLOCK) __attribute__((amdgpu_waves_per_eu(kPassWavesPerSimd)))
