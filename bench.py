@@ -71,12 +71,23 @@ WORKLOADS = {
 DEFAULT = "pairs_u32_2p28"
 
 
-def source_hash():
+def code_of(text):
+    """Source text without its comments and with runs of whitespace as one
+    space, so that a change to comments alone keeps the hash."""
+    import re
+    text = re.sub(r"/\*.*?\*/", " ", text, flags=re.S)
+    text = re.sub(r"//[^\n]*", " ", text)
+    return " ".join(text.split())
+
+
+def source_hash(csrc=CSRC):
+    """Hash of the kernel sources' code: the key that ties a recorded traffic
+    figure to the kernels it was measured on."""
     h = hashlib.sha256()
-    for f in sorted(os.listdir(CSRC)):
-        with open(os.path.join(CSRC, f), "rb") as fh:
+    for f in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, f), encoding="utf-8") as fh:
             h.update(f.encode())
-            h.update(fh.read())
+            h.update(code_of(fh.read()).encode())
     return h.hexdigest()[:16]
 
 

@@ -124,3 +124,14 @@ def test_bench_functions_read_only_defined_names():
 
     walk(top)
     assert not missing, missing
+
+
+def test_source_hash_ignores_comments_only(tmp_path):
+    import bench
+    src = tmp_path / "k.hip"
+    src.write_text("int f(int x) {\n    return x + 1;   // one more\n}\n")
+    h0 = bench.source_hash(str(tmp_path))
+    src.write_text("/* a block\n   comment */\nint f(int x) {\n  return x + 1;  // changed note\n}\n")
+    assert bench.source_hash(str(tmp_path)) == h0
+    src.write_text("int f(int x) {\n    return x + 2;\n}\n")
+    assert bench.source_hash(str(tmp_path)) != h0
