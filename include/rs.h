@@ -118,8 +118,13 @@ typedef enum rs_key_type {
  *          begin_bit == end_bit copies the input.
  * d_temp, temp_bytes: see the query idiom above.
  * Up to 16384 keys the whole sort runs in one workgroup in LDS (one launch,
- * the temp buffer is not touched); above, one digit-count launch and one
- * launch per digit pass.
+ * the temp buffer is not touched).  Above, a clear launch and one digit-count
+ * launch come first; then, up to 3 * 2^20 keys with two or more digit passes,
+ * the hybrid path ("第10章 并行模式：排序", 10.5, 策略2 混合排序): a pass on
+ * the top digit, then one workgroup per bucket sorting the lower digits in
+ * LDS, or, when a bucket holds more than 16384 keys, every LSD pass in one
+ * launch (the device decides; both launches are always enqueued); above
+ * that, one launch per digit pass.
  */
 rs_status rs_sort_keys_u32(const uint32_t *keys_in, uint32_t *keys_out, uint64_t n,
                            int begin_bit, int end_bit, void *d_temp, size_t *temp_bytes,
