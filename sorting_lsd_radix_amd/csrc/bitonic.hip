@@ -75,6 +75,87 @@ __global__ __launch_bounds__(kBitonicBlock) void bitonic_tile_kernel(
         keys_out[base + i] = s_key[static_cast<uint32_t>(s_item[i])];
 }
 
+// Full-width keys (begin_bit 0, end_bit 32): equal fields are equal keys, so
+// the network needs no positions and any order of equals is the stable one.
+// 256 threads hold the padded 1024-key tile in registers, four keys each:
+// element e = 4 * tid + r (wave w holds e in [256 w, 256 w + 256)).  Step
+// (k, j) pairs e with e ^ j: for j = 1, 2 both are in one thread's
+// registers; for j = 4 .. 128 the partner is lane ^ (j / 4) of the same wave
+// (DPP quad permutes for 1 and 2, a row rotate for 8, swizzles for 4 and
+// 16, a lane permute for 32); for j = 256, 512 it is in another wave, and
+// the step goes through LDS between two block barriers.  Element e keeps the
+// smaller of the pair when (e is the lower index) == (e & k == 0, the
+// ascending half of its bitonic sequence), the larger otherwise.
+constexpr int kBitonicRegThreads = 256;
+
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane distance");
+    if constexpr (M == 1) return __builtin_amdgcn_mov_dpp(x, 0xB1, 0xF, 0xF, false);   // quad_perm 1,0,3,2
+    else if constexpr (M == 2) return __builtin_amdgcn_mov_dpp(x, 0x4E, 0xF, 0xF, false);   // quad_perm 2,3,0,1
+    else if constexpr (M == 8) return __builtin_amdgcn_mov_dpp(x, 0x128, 0xF, 0xF, false);  // row_ror:8
+    else if constexpr (M == 4 || M == 16)   // swizzle, bitmask mode: lane ^ M within 32 lanes
+        return static_cast<uint32_t>(__builtin_amdgcn_ds_swizzle(static_cast<int>(x), 0x1F | (M << 10)));
+    else return __shfl_xor(x, 32, kWave);
+}
+
+__device__ __forceinline__ uint32_t keep(uint32_t x, uint32_t y, uint32_t e, uint32_t j, uint32_t k) {
+    const bool keep_min = ((e & j) == 0) == ((e & k) == 0);
+    return keep_min ? min(x, y) : max(x, y);
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_step(uint32_t (&x)[4], uint32_t e0, uint32_t* s) {
+    if constexpr (J >= 256) {
+        __syncthreads();   // the previous exchange's reads are done
+#pragma unroll
+        for (int r = 0; r < 4; ++r) s[e0 + r] = x[r];
+        __syncthreads();
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = keep(x[r], s[(e0 + r) ^ J], e0 + r, J, K);
+    } else if constexpr (J >= 4) {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) x[r] = keep(x[r], lane_xor<J / 4>(x[r]), e0 + r, J, K);
+    } else {
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+            if ((r & J) == 0) {
+                const uint32_t a = x[r], b = x[r + J];
+                const bool up = ((e0 + r) & K) == 0;
+                x[r] = up ? min(a, b) : max(a, b);
+                x[r + J] = up ? max(a, b) : min(a, b);
+            }
+        }
+    }
+}
+
+template <int K, int J>
+__device__ __forceinline__ void bitonic_merge(uint32_t (&x)[4], uint32_t e0, uint32_t* s) {
+    bitonic_step<K, J>(x, e0, s);
+    if constexpr (J > 1) bitonic_merge<K, J / 2>(x, e0, s);
+}
+
+template <int K>
+__device__ __forceinline__ void bitonic_network(uint32_t (&x)[4], uint32_t e0, uint32_t* s) {
+    bitonic_merge<K, K / 2>(x, e0, s);
+    if constexpr (K < kBitonicMax) bitonic_network<K * 2>(x, e0, s);
+}
+
+__global__ __launch_bounds__(kBitonicRegThreads) void bitonic_tile_u32_kernel(
+    const uint32_t* __restrict__ keys_in, uint32_t* __restrict__ keys_out, uint32_t n, uint32_t tile) {
+    __shared__ uint32_t s_x[kBitonicMax];
+    const uint32_t base = blockIdx.x * tile;
+    const uint32_t len = (n - base < tile) ? n - base : tile;
+    const uint32_t e0 = threadIdx.x * 4;
+    uint32_t x[4];
+#pragma unroll
+    for (int r = 0; r < 4; ++r) x[r] = (e0 + r < len) ? keys_in[base + e0 + r] : 0xFFFFFFFFu;   // pads sort last
+    bitonic_network<2>(x, e0, s_x);
+#pragma unroll
+    for (int r = 0; r < 4; ++r)
+        if (e0 + r < len) keys_out[base + e0 + r] = x[r];
+}
+
 }  // namespace
 
 hipError_t launch_bitonic(const uint32_t* keys_in, uint32_t* keys_out, uint32_t n, uint32_t tile,
@@ -87,8 +168,11 @@ hipError_t launch_bitonic(const uint32_t* keys_in, uint32_t* keys_out, uint32_t 
     const uint32_t shift = (width == 0) ? 0u : static_cast<uint32_t>(begin_bit);
     const uint32_t tiles = (n + tile - 1) / tile;
     timing_before(stream, RS_KERNEL_BITONIC);
-    bitonic_tile_kernel<<<dim3(tiles), kBitonicBlock, 0, stream>>>(keys_in, keys_out, n, tile, span,
-                                                                   shift, mask);
+    if (begin_bit == 0 && end_bit == 32)
+        bitonic_tile_u32_kernel<<<dim3(tiles), kBitonicRegThreads, 0, stream>>>(keys_in, keys_out, n, tile);
+    else
+        bitonic_tile_kernel<<<dim3(tiles), kBitonicBlock, 0, stream>>>(keys_in, keys_out, n, tile, span,
+                                                                       shift, mask);
     hipError_t e = hipGetLastError();
     timing_after(stream);
     return e;
