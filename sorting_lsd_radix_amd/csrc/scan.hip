@@ -77,7 +77,35 @@ __device__ uint32_t scan_look_back(uint64_t* states, uint32_t tile, uint32_t lan
 // its share of every row; wave 0 then scans the 128 (row, wave) totals in
 // that order, publishes the tile's sum, looks back and hands every wave its
 // offsets.
+//
+// Software-pipelined over a block's tiles: the next tile is taken during the
+// look-back and its loads are issued before this tile's stores.  One
+// counter tracks a wave's loads and stores together and in order, so a
+// wait for loads issued after the stores would also wait for the stores to
+// drain; issued before them, the next tile's data arrives while the stores
+// are still in flight.  The per-tile LDS words are double-buffered by the
+// parity of the block's tile count, so a wave that runs ahead to the next
+// tile never overwrites words a slower wave still reads.
 // ---------------------------------------------------------------------------
+__device__ __forceinline__ void scan_load_tile(__amdgpu_buffer_rsrc_t in_rsrc, uint32_t base, bool full,
+                                               uint32_t tid, uint32_t (&x)[kScanQuads][4]) {
+#pragma unroll
+    for (int q = 0; q < kScanQuads; ++q) {
+        const uint32_t e0 = base + (q * kScanBlock + tid) * 4;
+        if (full) {
+            const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(in_rsrc, static_cast<int>(e0 * 4u), 0, 2);
+            x[q][0] = v.x;
+            x[q][1] = v.y;
+            x[q][2] = v.z;
+            x[q][3] = v.w;
+        } else {
+#pragma unroll
+            for (int e = 0; e < 4; ++e)   // past n: 0 (the descriptor returns 0 there)
+                x[q][e] = __builtin_amdgcn_raw_buffer_load_b32(in_rsrc, static_cast<int>((e0 + e) * 4u), 0, 2);
+        }
+    }
+}
+
 template <bool INCLUSIVE>
 __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __restrict__ in,
                                                           uint32_t* __restrict__ out, uint32_t n,
@@ -87,9 +115,9 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
     constexpr int WAVES = kScanBlock / kWave;
     constexpr int PARTS = kScanQuads * WAVES;          // (row, wave) totals, row-major
     static_assert(PARTS % kWave == 0, "wave 0 scans the totals in lane-sized groups");
-    __shared__ uint32_t s_part[PARTS];                 // totals, then exclusive offsets in the tile
-    __shared__ uint32_t s_tile;
-    __shared__ uint32_t s_excl;
+    __shared__ uint32_t s_part[2][PARTS];              // totals, then exclusive offsets in the tile
+    __shared__ uint32_t s_tile[2];                     // [0]: the first tile; then the next tile
+    __shared__ uint32_t s_excl[2];
 
     const uint32_t tid = threadIdx.x;
     const uint32_t lane = tid & (kWave - 1);
@@ -100,30 +128,17 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
     const __amdgpu_buffer_rsrc_t out_rsrc =
         __builtin_amdgcn_make_buffer_rsrc(out, 0, static_cast<int>(n * 4u), kBufferWord3);
 
-    for (;;) {
-        if (tid == 0) s_tile = next_chunked_tile(sched, groups, chunk_log2, group, tiles);
-        __syncthreads();
-        const uint32_t tile = s_tile;
-        if (tile >= tiles) break;   // uniform
+    if (tid == 0) s_tile[1] = next_chunked_tile(sched, groups, chunk_log2, group, tiles);
+    __syncthreads();
+    uint32_t tile = s_tile[1];
+    if (tile >= tiles) return;   // uniform
+    uint32_t x[kScanQuads][4];
+    scan_load_tile(in_rsrc, tile * kScanTile, n - tile * kScanTile >= static_cast<uint32_t>(kScanTile), tid, x);
+
+    for (uint32_t it = 0;; ++it) {
+        const uint32_t buf = it & 1u;
         const uint32_t base = tile * kScanTile;
         const bool full = n - base >= static_cast<uint32_t>(kScanTile);
-
-        uint32_t x[kScanQuads][4];
-#pragma unroll
-        for (int q = 0; q < kScanQuads; ++q) {
-            const uint32_t e0 = base + (q * kScanBlock + tid) * 4;
-            if (full) {
-                const u32x4 v = __builtin_amdgcn_raw_buffer_load_b128(in_rsrc, static_cast<int>(e0 * 4u), 0, 2);
-                x[q][0] = v.x;
-                x[q][1] = v.y;
-                x[q][2] = v.z;
-                x[q][3] = v.w;
-            } else {
-#pragma unroll
-                for (int e = 0; e < 4; ++e)   // past n: 0 (the descriptor returns 0 there)
-                    x[q][e] = __builtin_amdgcn_raw_buffer_load_b32(in_rsrc, static_cast<int>((e0 + e) * 4u), 0, 2);
-            }
-        }
 
         // inclusive sums inside each vector, the vectors' totals scanned over the wave
         uint32_t wave_excl[kScanQuads];
@@ -134,18 +149,20 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
             x[q][3] += x[q][2];
             const uint32_t inc = wave_inclusive_sum(x[q][3]);
             wave_excl[q] = inc - x[q][3];
-            if (lane == kWave - 1) s_part[q * WAVES + wave] = inc;
+            if (lane == kWave - 1) s_part[buf][q * WAVES + wave] = inc;
         }
         __syncthreads();
 
         if (wave == 0) {
+            // the next tile, in flight during the scan of the totals and the look-back
+            const uint32_t next = (tid == 0) ? next_chunked_tile(sched, groups, chunk_log2, group, tiles) : 0u;
             // exclusive offsets of the (row, wave) parts inside the tile
             uint32_t carry = 0;
 #pragma unroll
             for (int g = 0; g < PARTS / kWave; ++g) {
-                const uint32_t v = s_part[g * kWave + lane];
+                const uint32_t v = s_part[buf][g * kWave + lane];
                 const uint32_t inc = wave_inclusive_sum(v);
-                s_part[g * kWave + lane] = carry + inc - v;
+                s_part[buf][g * kWave + lane] = carry + inc - v;
                 carry += __shfl(inc, kWave - 1, kWave);
             }
             const uint32_t tile_total = carry;
@@ -156,26 +173,39 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
                 excl = scan_look_back(states, tile, lane);
                 if (lane == 0) store_state64(&states[tile], kScanPrefix | static_cast<uint32_t>(excl + tile_total));
             }
-            if (lane == 0) s_excl = excl;
+            if (lane == 0) {
+                s_excl[buf] = excl;
+                s_tile[buf] = next;
+            }
         }
         __syncthreads();
-        const uint32_t excl = s_excl;
+        const uint32_t excl = s_excl[buf];
+        const uint32_t next = s_tile[buf];
+
+        // this tile's sums stay in x_out; x takes the next tile's loads
+        uint32_t x_out[kScanQuads][4];
+#pragma unroll
+        for (int q = 0; q < kScanQuads; ++q)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) x_out[q][e] = x[q][e];
+        if (next < tiles)   // uniform
+            scan_load_tile(in_rsrc, next * kScanTile, n - next * kScanTile >= static_cast<uint32_t>(kScanTile), tid, x);
 
 #pragma unroll
         for (int q = 0; q < kScanQuads; ++q) {
-            const uint32_t off = excl + s_part[q * WAVES + wave] + wave_excl[q];
+            const uint32_t off = excl + s_part[buf][q * WAVES + wave] + wave_excl[q];
             u32x4 v;
-            // x[q][e] holds the inclusive sum of the vector's elements 0..e
+            // x_out[q][e] holds the inclusive sum of the vector's elements 0..e
             if (INCLUSIVE) {
-                v.x = off + x[q][0];
-                v.y = off + x[q][1];
-                v.z = off + x[q][2];
-                v.w = off + x[q][3];
+                v.x = off + x_out[q][0];
+                v.y = off + x_out[q][1];
+                v.z = off + x_out[q][2];
+                v.w = off + x_out[q][3];
             } else {
                 v.x = off;
-                v.y = off + x[q][0];
-                v.z = off + x[q][1];
-                v.w = off + x[q][2];
+                v.y = off + x_out[q][0];
+                v.z = off + x_out[q][1];
+                v.w = off + x_out[q][2];
             }
             const uint32_t e0 = base + (q * kScanBlock + tid) * 4;
             if (full) {
@@ -187,7 +217,8 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
                 __builtin_amdgcn_raw_buffer_store_b32(v.w, out_rsrc, static_cast<int>((e0 + 3) * 4u), 0, 0);
             }
         }
-        // s_part and s_excl are rewritten only after the next loop-top barrier
+        if (next >= tiles) break;   // uniform
+        tile = next;
     }
 }
 
