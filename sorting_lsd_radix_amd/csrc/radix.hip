@@ -252,10 +252,8 @@ __global__ __launch_bounds__(kUpBlock) void upsweep64_kernel(const uint32_t* __r
     const uint32_t end = (begin + per_block < nvec) ? begin + per_block : nvec;
     const u32x4* k4 = reinterpret_cast<const u32x4*>(keys);
     const u32x4* h4 = reinterpret_cast<const u32x4*>(keys_hi);
-    for (uint32_t i = begin + threadIdx.x; i < end; i += kUpBlock) {
-        const u32x4 q = __builtin_nontemporal_load(&k4[i]);
+    auto count_vec = [&](const u32x4& q, const u32x4& h) {
         if (SOA) {
-            const u32x4 h = __builtin_nontemporal_load(&h4[i]);
             count_key64<XF>(s_hist, (static_cast<uint64_t>(h.x) << 32) | q.x, pd, sub);
             count_key64<XF>(s_hist, (static_cast<uint64_t>(h.y) << 32) | q.y, pd, sub);
             count_key64<XF>(s_hist, (static_cast<uint64_t>(h.z) << 32) | q.z, pd, sub);
@@ -264,6 +262,22 @@ __global__ __launch_bounds__(kUpBlock) void upsweep64_kernel(const uint32_t* __r
             count_key64<XF>(s_hist, (static_cast<uint64_t>(q.y) << 32) | q.x, pd, sub);
             count_key64<XF>(s_hist, (static_cast<uint64_t>(q.w) << 32) | q.z, pd, sub);
         }
+    };
+    // four rows of kUpBlock vectors in flight at a time, as the 4-byte upsweep
+    uint32_t i = begin + threadIdx.x;
+    for (; i + 3 * kUpBlock < end; i += 4 * kUpBlock) {
+        u32x4 q[4], h[4];
+#pragma unroll
+        for (int u = 0; u < 4; ++u) {
+            q[u] = __builtin_nontemporal_load(&k4[i + u * kUpBlock]);
+            h[u] = SOA ? __builtin_nontemporal_load(&h4[i + u * kUpBlock]) : q[u];
+        }
+#pragma unroll
+        for (int u = 0; u < 4; ++u) count_vec(q[u], h[u]);
+    }
+    for (; i < end; i += kUpBlock) {
+        const u32x4 q = __builtin_nontemporal_load(&k4[i]);
+        count_vec(q, SOA ? __builtin_nontemporal_load(&h4[i]) : q);
     }
     if (blockIdx.x == 0 && threadIdx.x < n - nvec * PER_VEC) {
         const uint32_t j = nvec * PER_VEC + threadIdx.x;
