@@ -116,7 +116,7 @@ __global__ __launch_bounds__(kScanBlock) void scan_kernel(const uint32_t* __rest
     constexpr int PARTS = kScanQuads * WAVES;          // (row, wave) totals, row-major
     static_assert(PARTS % kWave == 0, "wave 0 scans the totals in lane-sized groups");
     __shared__ uint32_t s_part[2][PARTS];              // totals, then exclusive offsets in the tile
-    __shared__ uint32_t s_tile[2];                     // [0]: the first tile; then the next tile
+    __shared__ uint32_t s_tile[2];                     // [1]: the first tile; [it & 1]: the tile taken in iteration it
     __shared__ uint32_t s_excl[2];
 
     const uint32_t tid = threadIdx.x;
