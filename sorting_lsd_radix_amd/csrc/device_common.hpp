@@ -58,10 +58,14 @@ __device__ __forceinline__ uint32_t fetch_add_agent(uint32_t* p, uint32_t v) {
 // consecutive tiles, and group g owns the chunks g, g + groups, g + 2 groups,
 // ...; its blocks take that sequence in order from one counter.  Neighbouring
 // tiles thus run at the same time on one XCD, and the cache lines their
-// output runs share are merged in that XCD's L2 before they reach memory.  A block starts each tile it takes at once, every group has a
-// block, and a group hands out its tiles in increasing order.  So the
-// smallest unfinished tile is either running (every earlier tile is done,
-// and its look-back ends) or not yet handed out, and then every tile its
+// output runs share are merged in that XCD's L2 before they reach memory.
+// A block starts each tile it takes at once (the pipelined scan takes its
+// next tile during the current one's look-back and starts it when the
+// current one, a smaller tile, is done), every group has a block, and a
+// group hands out its tiles in increasing order.  So the smallest unfinished
+// tile is either running (every earlier tile is done, and its look-back
+// ends), or taken by a block whose current tile is smaller, hence done, so
+// that it starts at once, or not yet handed out, and then every tile its
 // group has handed out is smaller, hence done, and a block of that group is
 // free to take it: look-back always makes progress.
 // Layout: sched[g] = tiles taken by group g.

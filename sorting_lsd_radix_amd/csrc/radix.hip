@@ -24,9 +24,12 @@
 //    banks;
 //  * the tile is re-laid out in LDS in digit order so that each digit's run
 //    is written to HBM with consecutive addresses;
-//  * tile ids come from an atomic counter, so a tile only ever waits on
-//    tiles that are already running; state words are read and written at
-//    agent scope because tiles on different XCDs sit behind different L2s;
+//  * tile ids come from one atomic counter per XCD group, each handing out
+//    its interleaved chunks of consecutive tiles in order, so a tile only
+//    waits on smaller tiles, which blocks of their groups take in turn
+//    (next_chunked_tile states the residency this needs); state words are
+//    read and written at agent scope because tiles on different XCDs sit
+//    behind different L2s;
 //  * every key type and direction is a sign-dependent XOR of the key's words
 //    (KeyXform), applied on the first pass's load and undone on the last
 //    pass's store; the passes in between move the transformed patterns
