@@ -286,7 +286,7 @@ hipError_t launch_compact(const float* in, float* out, uint32_t* d_count, uint32
     uint32_t* states = reinterpret_cast<uint32_t*>(base + L.states);
     hipError_t e = launch_fill_zero(sched, L.total / 4, stream, RS_KERNEL_COMPACT_INIT);
     if (e != hipSuccess) return e;
-    const TileGrid g = tile_grid(L.tiles, compact_resident());
+    const TileGrid g = tile_grid(L.tiles, compact_resident(), kStreamChunk);
     timing_before(stream, RS_KERNEL_COMPACT);
     compact_kernel<<<dim3(g.grid), kCompBlock, 0, stream>>>(
         reinterpret_cast<const uint32_t*>(in), reinterpret_cast<uint32_t*>(out), d_count, n,

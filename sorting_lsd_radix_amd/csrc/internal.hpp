@@ -24,7 +24,14 @@ int device_cus();
 struct TileGrid {
     uint32_t grid, groups, chunk_log2;
 };
-TileGrid tile_grid(uint32_t tiles, uint32_t resident);
+TileGrid tile_grid(uint32_t tiles, uint32_t resident, uint32_t max_chunk);
+// Chunk caps.  Sort passes: 16 tiles (with 32 blocks per XCD each XCD then
+// works on two chunks at once; 2^28 pair pass 0.871 -> 0.848 ms, keys-only
+// sort 2.10 -> 2.00 ms against 32; chunks of 8, 12, 20 and 24 tiles were all
+// slower than 16).  Compaction, scan and select: 32 (their 64-tile look-back
+// steps do not gain from shorter chains, and 16 made them 3-8 % slower).
+constexpr uint32_t kPassChunk = 16;
+constexpr uint32_t kStreamChunk = 32;
 
 // ---- radix sort ---------------------------------------------------------------
 

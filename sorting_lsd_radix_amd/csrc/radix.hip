@@ -101,7 +101,6 @@ static_assert(kHybridMaxN / kSortTile <= kWideMaxTiles, "the multi-pass fallback
 // tiles (1 % faster than 2 there, 1-2 % slower elsewhere).
 constexpr int kSortLookback = 2;
 constexpr int kPairsLookback = 1;
-constexpr int kChunk = 32;             // consecutive tiles per XCD chunk
 constexpr int kGroups = 8;             // XCDs
 // Cache-policy operand of a buffer access: the non-temporal bit.
 constexpr int kNonTemporal = 2;
@@ -1278,7 +1277,7 @@ template <int BLOCK, int ITEMS, int LOOKBACK, bool PAIRS, bool XI, bool XO, bool
 hipError_t launch_pass_t(const PassArgs& a, hipStream_t s) {
     auto kern = onesweep_kernel<BLOCK, ITEMS, LOOKBACK, PAIRS, XI, XO, KEY64, false, WIDE>;
     static const uint32_t resident = resident_blocks(kern, BLOCK);   // one-time init
-    const TileGrid g = tile_grid(a.tiles, resident);
+    const TileGrid g = tile_grid(a.tiles, resident, kPassChunk);
     PassArgs b = a;
     b.groups = g.groups;
     b.chunk_log2 = g.chunk_log2;
@@ -1430,7 +1429,7 @@ hipError_t launch_upsweep(const SortIo& io, const SortKind& kind, const PassDigi
 
 }  // namespace
 
-TileGrid tile_grid(uint32_t tiles, uint32_t resident) {
+TileGrid tile_grid(uint32_t tiles, uint32_t resident, uint32_t max_chunk) {
     TileGrid g{};
     g.grid = tiles < resident ? tiles : resident;
     if (g.grid == 0) g.grid = 1;
@@ -1438,7 +1437,7 @@ TileGrid tile_grid(uint32_t tiles, uint32_t resident) {
     // the blocks per group, capped
     g.groups = g.grid < static_cast<uint32_t>(kGroups) ? g.grid : static_cast<uint32_t>(kGroups);
     g.chunk_log2 = 0;
-    while ((2u << g.chunk_log2) <= g.grid / g.groups && (2u << g.chunk_log2) <= kChunk) ++g.chunk_log2;
+    while ((2u << g.chunk_log2) <= g.grid / g.groups && (2u << g.chunk_log2) <= max_chunk) ++g.chunk_log2;
     return g;
 }
 

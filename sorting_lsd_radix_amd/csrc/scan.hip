@@ -555,7 +555,7 @@ template <int TYPE, bool PARTITION, bool PAIRS>
 hipError_t launch_select_t(const SelectArgs& a, hipStream_t s) {
     auto kern = select_kernel<TYPE, PARTITION, PAIRS>;
     static const uint32_t resident = resident_of(kern);   // one-time init
-    const TileGrid g = tile_grid(a.tiles, resident);
+    const TileGrid g = tile_grid(a.tiles, resident, kStreamChunk);
     SelectArgs b = a;
     b.groups = g.groups;
     b.chunk_log2 = g.chunk_log2;
@@ -587,7 +587,7 @@ hipError_t launch_scan(const uint32_t* in, uint32_t* out, uint32_t n, bool inclu
     if (e != hipSuccess) return e;
     auto kern = inclusive ? scan_kernel<true> : scan_kernel<false>;
     static const uint32_t resident = resident_of(scan_kernel<false>);   // same shape either way
-    const TileGrid g = tile_grid(L.tiles, resident);
+    const TileGrid g = tile_grid(L.tiles, resident, kStreamChunk);
     timing_before(stream, RS_KERNEL_SCAN);
     kern<<<dim3(g.grid), kScanBlock, 0, stream>>>(in, out, n, L.tiles, states, sched, g.groups, g.chunk_log2);
     e = hipGetLastError();
