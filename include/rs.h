@@ -46,15 +46,19 @@
  *    hold 30-bit counts beside 2 status bits.  Sorts of 64-bit keys and
  *    two-key sorts take n < 2^29, which keeps every byte offset into an
  *    array of 8-byte keys below 2^32.
- *  - Scheduling assumption of the persistent kernels (sort passes and
- *    compaction): their grid never exceeds the number of blocks that fit on
- *    the device at once, tiles are handed out in increasing order per group
- *    of blocks, and a tile waits only on tiles with smaller ids.  Progress
- *    needs at least one block of every group (up to 8) to be resident, which
- *    holds whenever the kernel can start on the device at all (other work on
- *    other streams only delays blocks that have not started; blocks that
- *    started keep running).  A device partitioned so that a kernel's blocks
- *    could be preempted indefinitely is outside this contract.
+ *  - Scheduling assumption of the persistent kernels (sort passes,
+ *    compaction, scan, select and partition): their grid never exceeds the
+ *    number of blocks that fit on the device at once, tiles are handed out
+ *    in increasing order per group of blocks (one group per XCD), and a tile
+ *    waits only on tiles with smaller ids.  Progress needs at least one block
+ *    of every group (up to 8) to become resident.  That holds on an
+ *    otherwise idle device and beside kernels that finish without waiting
+ *    on this one (they only delay blocks that have not started; blocks that
+ *    started keep running).  Two such kernels started at the same time on
+ *    different streams of one device, each holding every CU of some XCD
+ *    while waiting for the other to free it, or a device partitioned so
+ *    that a kernel's blocks could be preempted indefinitely, are outside
+ *    this contract.
  */
 #ifndef RS_H
 #define RS_H
