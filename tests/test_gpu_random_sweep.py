@@ -9,13 +9,19 @@ the small LSD shapes with both look-back forms are all reached, a key type
 distribution (typed samples with extremes and specials, a narrow range that
 crowds the top digit, a handful of values, an already sorted input), and
 sorts keys only or keys with index values.
+
+A second sweep draws prefix sums, selects and partitions: sizes log-uniform
+up to 2^23 (one case in four between 2^20 and 2^24, so tiles run in several
+rounds of the persistent grid), any of the six comparisons against a random
+threshold on u32, i32 or f32 elements (floats from random bit patterns, so
+NaNs, infinities and signed zeros occur), with or without index values.
 """
 import numpy as np
 import pytest
 
 import oracle
 import pins
-from gpu_helpers import gpu_sort_typed
+from gpu_helpers import _raw, gpu_scan, gpu_select, gpu_sort_typed
 
 pytestmark = pytest.mark.gpu
 
@@ -70,3 +76,42 @@ def test_random_typed_sort(case):
         k = gpu_sort_typed(keys, None, descending, b, e)
         rk = oracle.sort_typed(keys, None, b, e, descending)
         assert np.array_equal(bits(k), bits(rk))
+
+
+STREAM_CASES = 48
+OPS = ["<", "<=", ">", ">=", "==", "!="]
+
+
+@pytest.mark.parametrize("case", range(STREAM_CASES))
+def test_random_scan_select_partition(case):
+    r = np.random.default_rng(3000 + case)
+    if case % 4:
+        n = int(np.exp(r.uniform(0.0, np.log(1 << 23))))
+    else:
+        n = int(r.integers(1 << 20, 1 << 24))
+    kind = case % 3
+    if kind == 0:
+        inclusive = bool(r.random() < 0.5)
+        print("stream case %d: scan n=%d inclusive=%d" % (case, n, inclusive), flush=True)
+        x = r.integers(0, 1 << 32, n, dtype=np.uint64).astype(np.uint32)
+        assert np.array_equal(gpu_scan(x, inclusive), oracle.scan_u32(x, inclusive))
+        return
+    partition = kind == 2
+    dtype = [np.uint32, np.int32, np.float32][int(r.integers(0, 3))]
+    op = OPS[int(r.integers(0, len(OPS)))]
+    x = (pins.random_float_patterns(r, n).view(np.float32) if dtype == np.float32
+         else pins.typed_sample(r, dtype, n))
+    t = {np.uint32: np.uint32(r.integers(0, 1 << 32, dtype=np.uint64)),
+         np.int32: np.int32(r.integers(-2 ** 31, 2 ** 31 - 1)),
+         np.float32: np.float32(r.standard_normal())}[dtype]
+    vals = np.arange(n, dtype=np.uint32) if r.random() < 0.5 else None
+    print("stream case %d: %s n=%d %s x %s %r vals=%d" % (
+        case, "partition" if partition else "select", n, np.dtype(dtype).name, op, t,
+        vals is not None), flush=True)
+    o, v, c = gpu_select(x, op, t, vals, partition)
+    ref = oracle.select(x, op, t, vals, partition)
+    assert c == ref[-1]
+    m = n if partition else c
+    assert np.array_equal(_raw(o)[:m], _raw(ref[0])[:m])
+    if vals is not None:
+        assert np.array_equal(v[:m], ref[1][:m])
