@@ -28,8 +28,10 @@ TileGrid tile_grid(uint32_t tiles, uint32_t resident, uint32_t max_chunk);
 // Chunk caps.  Sort passes: 16 tiles (with 32 blocks per XCD each XCD then
 // works on two chunks at once; 2^28 pair pass 0.871 -> 0.848 ms, keys-only
 // sort 2.10 -> 2.00 ms against 32; chunks of 8, 12, 20 and 24 tiles were all
-// slower than 16).  Compaction, scan and select: 32 (their 64-tile look-back
-// steps do not gain from shorter chains, and 16 made them 3-8 % slower).
+// slower than 16); also the select with values, whose 16384-element tiles
+// make twice as many tiles.  Compaction, scan and the select without values
+// (32768-element tiles): 32 (their 64-tile look-back steps do not gain from
+// shorter chains, and 16 made the compaction and scan 3-8 % slower).
 constexpr uint32_t kPassChunk = 16;
 constexpr uint32_t kStreamChunk = 32;
 
