@@ -486,20 +486,25 @@ __global__ __launch_bounds__(kSelBlock) void count_kept_kernel(const uint32_t* _
     const uint32_t nvec = n / 4;
     const u32x4* in4 = reinterpret_cast<const u32x4*>(in);
     uint32_t c = 0;
-    const uint32_t stride = gridDim.x * kSelBlock;
-    // four independent 16-byte loads in flight per thread (nvec < 2^28, so
-    // no index below wraps)
+    // one contiguous chunk of 16-byte vectors per block, four rows of the
+    // block in flight at a time (nvec < 2^28, so no index below wraps)
     constexpr int kInFlight = 4;
-    for (uint32_t i = blockIdx.x * kSelBlock + tid; i < nvec; i += kInFlight * stride) {
+    const uint32_t per_block = (nvec + gridDim.x - 1) / gridDim.x;
+    const uint32_t begin = blockIdx.x * per_block;
+    const uint32_t end = (begin + per_block < nvec) ? begin + per_block : nvec;
+    uint32_t i = begin + tid;
+    for (; i + (kInFlight - 1) * kSelBlock < end; i += kInFlight * kSelBlock) {
         u32x4 q[kInFlight];
 #pragma unroll
-        for (int u = 0; u < kInFlight; ++u)
-            if (i + u * stride < nvec) q[u] = __builtin_nontemporal_load(&in4[i + u * stride]);
+        for (int u = 0; u < kInFlight; ++u) q[u] = __builtin_nontemporal_load(&in4[i + u * kSelBlock]);
 #pragma unroll
         for (int u = 0; u < kInFlight; ++u)
-            if (i + u * stride < nvec)
-                c += keeps<TYPE>(q[u].x, pred) + keeps<TYPE>(q[u].y, pred) + keeps<TYPE>(q[u].z, pred) +
-                     keeps<TYPE>(q[u].w, pred);
+            c += keeps<TYPE>(q[u].x, pred) + keeps<TYPE>(q[u].y, pred) + keeps<TYPE>(q[u].z, pred) +
+                 keeps<TYPE>(q[u].w, pred);
+    }
+    for (; i < end; i += kSelBlock) {
+        const u32x4 q = __builtin_nontemporal_load(&in4[i]);
+        c += keeps<TYPE>(q.x, pred) + keeps<TYPE>(q.y, pred) + keeps<TYPE>(q.z, pred) + keeps<TYPE>(q.w, pred);
     }
     if (blockIdx.x == 0 && tid < n - nvec * 4) c += keeps<TYPE>(in[nvec * 4 + tid], pred);
     c = __shfl(wave_inclusive_sum(c), kWave - 1, kWave);
